@@ -1,0 +1,338 @@
+// Column-by-column quantization with OBS feedback and lazy block updates.
+//
+// [teardown] Algorithm 1 and [derivation] section 10: for each block
+// [i, i2) of the processing order and each column j in it
+//   q = Delta (clip(round(w / Delta) + z, 0, 2^b - 1) - z)      (eq. (36))
+//   eta = (w - q) / R_jj,  W[:, j:i2] -= eta R[j, j:i2]           (eq. (42))
+// then W[:, i2:] -= E R[i:i2, i2:] with E = [eta_i .. eta_{i2-1}]  (eq. (46)).
+// Dynamic groups refit Delta, z at each group start on the current working
+// weights ([derivation] 8.3/8.4); the whole-row grid is fitted once on the
+// original row ([derivation] section 10 pseudocode).
+//
+// Layout: the fp32 working copy is kept feature-major, WT[j][r] = W_work[r][j]
+// (column j of the processing order is one contiguous vector over the m
+// output rows), so reading a column, writing its codes and eta, and the
+// lazy update all stream contiguous memory.
+//
+// Chain kernel: one thread per output row (rows are independent given R and
+// their grids, [derivation] 2.3), the block's 128 columns in registers; the
+// R entries are wave-uniform loads.
+// Lazy update: v_mfma_f32_16x16x4_f32 (exact fp32 products, fp32 sums).
+#include <algorithm>
+
+#include "common.h"
+
+namespace gptq {
+namespace {
+
+constexpr int kB = 128;   // largest block handled by one chain launch
+constexpr int kSB = 32;   // sub-block held in registers
+
+__device__ inline float to_f32(float x) { return x; }
+__device__ inline float to_f32(uint16_t x) { return __uint_as_float(uint32_t(x) << 16); }
+
+// Min-max grid widened to contain 0 (so z represents 0 exactly); a flat
+// (all-zero) range becomes [-1, 1].  Delta = (hi - lo) / (2^b - 1),
+// z = round(-lo / Delta), all in IEEE fp32.
+__device__ inline void fit_grid(float lo, float hi, float maxq, float& scale,
+                                float& zero) {
+  if (hi == lo) {
+    lo = -1.0f;
+    hi = 1.0f;
+  }
+  scale = (hi - lo) / maxq;
+  zero = fminf(fmaxf(rintf(-lo / scale), 0.0f), maxq);
+}
+
+// Whole-row grid on the original weights: one wave per row.
+template <class T>
+__global__ __launch_bounds__(64) void fit_rows_kernel(
+    const T* __restrict__ W, int64_t d, int64_t ldw, float maxq,
+    float* __restrict__ scale, uint8_t* __restrict__ zero) {
+  const int64_t r = blockIdx.x;
+  float lo = 0.0f, hi = 0.0f;
+  for (int64_t c = threadIdx.x; c < d; c += 64) {
+    const float x = to_f32(W[r * ldw + c]);
+    lo = fminf(lo, x);
+    hi = fmaxf(hi, x);
+  }
+  for (int o = 32; o > 0; o >>= 1) {
+    lo = fminf(lo, __shfl_xor(lo, o));
+    hi = fmaxf(hi, __shfl_xor(hi, o));
+  }
+  if (threadIdx.x == 0) {
+    float s, z;
+    fit_grid(lo, hi, maxq, s, z);
+    scale[r] = s;
+    zero[r] = static_cast<uint8_t>(z);
+  }
+}
+
+__global__ void pinv_kernel(const int32_t* __restrict__ perm, int64_t d,
+                            int32_t* __restrict__ pinv) {
+  const int64_t j = int64_t(blockIdx.x) * blockDim.x + threadIdx.x;
+  if (j < d) pinv[perm[j]] = static_cast<int32_t>(j);
+}
+
+// WT[j][r] = dead[perm[j]] ? 0 : W[r][perm[j]]  via 64x64 LDS tiles.
+template <class T>
+__global__ __launch_bounds__(256) void init_work_kernel(
+    const T* __restrict__ W, int64_t m, int64_t d, int64_t ldw,
+    const int32_t* __restrict__ perm, const uint8_t* __restrict__ dead,
+    float* __restrict__ WT) {
+  __shared__ float tile[64][65];
+  const int64_t r0 = int64_t(blockIdx.x) * 64, j0 = int64_t(blockIdx.y) * 64;
+  const int lx = threadIdx.x & 63, ly = threadIdx.x >> 6;
+  const int64_t j = j0 + lx;
+  int64_t src = -1;
+  if (j < d) {
+    const int32_t p = perm[j];
+    if (!dead[p]) src = p;
+  }
+  for (int y = ly; y < 64; y += 4) {
+    const int64_t r = r0 + y;
+    tile[y][lx] = (r < m && src >= 0) ? to_f32(W[r * ldw + src]) : 0.0f;
+  }
+  __syncthreads();
+  for (int y = ly; y < 64; y += 4) {
+    const int64_t jj = j0 + y, r = r0 + lx;
+    if (jj < d && r < m) WT[jj * m + r] = tile[lx][y];
+  }
+}
+
+// Transposed diagonal blocks of R: RbT[blk][c][k] = R[i + k][i + c] for the
+// block starting at i = blk * bi (k <= c < bw), 0 elsewhere.  Column c of a
+// block's R is then contiguous for the batched in-block update below.
+__global__ __launch_bounds__(256) void rbt_kernel(const float* __restrict__ R,
+                                                  int64_t d, int bi,
+                                                  float* __restrict__ RbT) {
+  const int64_t blk = blockIdx.y;
+  const int64_t i = blk * bi;
+  const int bw = static_cast<int>(min<int64_t>(bi, d - i));
+  for (int e = threadIdx.x + blockIdx.x * 256; e < bi * bi; e += 256 * gridDim.x) {
+    const int c = e / bi, k = e % bi;
+    RbT[blk * bi * bi + e] = (k <= c && c < bw) ? R[(i + k) * d + i + c] : 0.0f;
+  }
+}
+
+// One block [i0, i0 + bw) of the column loop for all rows, one thread per
+// output row.  The block is processed in sub-blocks of up to kSB columns held
+// in registers; the rest of the block sits in lane-private LDS slots and
+// receives each sub-block's feedback in one batch (the in-block step of the
+// column loop applied with lazy batching inside the block).  FS: a dynamic
+// group can only start at sub-block offsets that are multiples of FS (0 = the
+// whole-row grid, no refits).  Groups that start inside a sub-block end
+// inside it (checked on the host), so every fit sees fully compensated
+// columns.
+template <int FS>
+__global__ __launch_bounds__(64) void chain_kernel(
+    float* __restrict__ WT, int64_t m, int64_t d, const float* __restrict__ R,
+    const float* __restrict__ RbT, int64_t i0, int bw, int sb, int bi,
+    float maxq, int64_t gsize, float* __restrict__ scalesP,
+    uint8_t* __restrict__ zerosP, uint8_t* __restrict__ codesP,
+    float* __restrict__ E) {
+  __shared__ float rows[kB][64];
+  const int lane = threadIdx.x;
+  const int64_t r = int64_t(blockIdx.x) * 64 + lane;
+  const bool act = r < m;
+  const int64_t rr = act ? r : 0;
+  for (int c = 0; c < bw; ++c) rows[c][lane] = WT[(i0 + c) * m + rr];
+  float scale = 1.0f, zero = 0.0f;
+  if (FS == 0) {
+    scale = scalesP[rr];
+    zero = static_cast<float>(zerosP[rr]);
+  }
+  for (int s0 = 0; s0 < bw; s0 += sb) {
+    const int sw = min(sb, bw - s0);
+    float w[kSB], eta[kSB];
+#pragma unroll
+    for (int k = 0; k < kSB; ++k) {
+      w[k] = (k < sw) ? rows[s0 + k][lane] : 0.0f;
+      eta[k] = 0.0f;
+    }
+#pragma unroll
+    for (int k = 0; k < kSB; ++k) {
+      if (k < sw) {
+        const int64_t col = i0 + s0 + k;
+        if (FS > 0 && (k % (FS > 0 ? FS : 1)) == 0 && (col % gsize) == 0) {
+          const int64_t gend = min(col + gsize, d);
+          float lo = 0.0f, hi = 0.0f;
+#pragma unroll
+          for (int c = k; c < kSB; ++c)
+            if (c < sw && col - k + c < gend) {
+              lo = fminf(lo, w[c]);
+              hi = fmaxf(hi, w[c]);
+            }
+          for (int c = s0 + sw; c < bw && i0 + c < gend; ++c) {
+            const float x = rows[c][lane];
+            lo = fminf(lo, x);
+            hi = fmaxf(hi, x);
+          }
+          for (int64_t cc = i0 + bw; cc < gend; ++cc) {
+            const float x = WT[cc * m + rr];
+            lo = fminf(lo, x);
+            hi = fmaxf(hi, x);
+          }
+          fit_grid(lo, hi, maxq, scale, zero);
+          if (act) {
+            scalesP[(col / gsize) * m + r] = scale;
+            zerosP[(col / gsize) * m + r] = static_cast<uint8_t>(zero);
+          }
+        }
+        const float* Rj = R + col * d + (col - k);   // row col, from the sub-block start
+        const float x = w[k];
+        const float c = fminf(fmaxf(rintf(x / scale) + zero, 0.0f), maxq);
+        const float q = scale * (c - zero);
+        eta[k] = (x - q) / Rj[k];
+        if (act) {
+          codesP[col * m + r] = static_cast<uint8_t>(c);
+          E[(s0 + k) * m + r] = eta[k];
+        }
+#pragma unroll
+        for (int k2 = k + 1; k2 < kSB; ++k2)
+          if (k2 < sw) w[k2] = fmaf(-eta[k], Rj[k2], w[k2]);
+      }
+    }
+    // feedback of this sub-block into the rest of the block
+    const float* rbt = RbT + (i0 / bi) * int64_t(bi) * bi;
+    for (int c = s0 + sw; c < bw; ++c) {
+      const float* rt = rbt + int64_t(c) * bi + s0;   // rt[k] = R[i0+s0+k][i0+c]
+      float x = rows[c][lane];
+#pragma unroll
+      for (int k = 0; k < kSB; ++k)
+        if (k < sw) x = fmaf(-eta[k], rt[k], x);
+      rows[c][lane] = x;
+    }
+  }
+}
+
+// WT[i2 + t][r] -= sum_k R[i0 + k][i2 + t] * E[k][r]   (t < d - i2, r < m).
+// 256 threads = 2 x 2 waves, each a 64 (t) x 64 (r) tile of 4 x 4
+// 16x16 MFMA blocks.  Lane l feeds A[t = l%16][k = l/16] and
+// B[k = l/16][r = l%16]; it receives D[t = 4(l/16) + v][r = l%16].
+__global__ __launch_bounds__(256) void lazy_update_kernel(
+    float* __restrict__ WT, int64_t m, int64_t d, const float* __restrict__ R,
+    int64_t i0, int bw, const float* __restrict__ E) {
+  const int64_t i2 = i0 + bw, nT = d - i2;
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int64_t t0 = int64_t(blockIdx.y) * 128 + (wave >> 1) * 64;
+  const int64_t r0 = int64_t(blockIdx.x) * 128 + (wave & 1) * 64;
+  const int lr = lane & 15, lk = lane >> 4;
+  f32x4 acc[4][4];
+#pragma unroll
+  for (int a = 0; a < 4; ++a)
+#pragma unroll
+    for (int b = 0; b < 4; ++b) acc[a][b] = f32x4{0.f, 0.f, 0.f, 0.f};
+  for (int k0 = 0; k0 < bw; k0 += 4) {
+    const int k = k0 + lk;
+    const bool kv = k < bw;
+    float av[4], bv[4];
+#pragma unroll
+    for (int a = 0; a < 4; ++a) {
+      const int64_t t = t0 + 16 * a + lr;
+      av[a] = (kv && t < nT) ? R[(i0 + k) * d + i2 + t] : 0.0f;
+    }
+#pragma unroll
+    for (int b = 0; b < 4; ++b) {
+      const int64_t rr = r0 + 16 * b + lr;
+      bv[b] = (kv && rr < m) ? E[int64_t(k) * m + rr] : 0.0f;
+    }
+#pragma unroll
+    for (int a = 0; a < 4; ++a)
+#pragma unroll
+      for (int b = 0; b < 4; ++b)
+        acc[a][b] = __builtin_amdgcn_mfma_f32_16x16x4f32(av[a], bv[b], acc[a][b], 0, 0, 0);
+  }
+#pragma unroll
+  for (int a = 0; a < 4; ++a)
+#pragma unroll
+    for (int b = 0; b < 4; ++b)
+#pragma unroll
+      for (int v = 0; v < 4; ++v) {
+        const int64_t t = t0 + 16 * a + 4 * lk + v;
+        const int64_t rr = r0 + 16 * b + lr;
+        if (t < nT && rr < m) WT[(i2 + t) * m + rr] -= acc[a][b][v];
+      }
+}
+
+unsigned cdiv(int64_t a, int64_t b) { return static_cast<unsigned>((a + b - 1) / b); }
+
+}  // namespace
+
+gptq_status launch_fit_rows(const void* W, gptq_dtype dt, int64_t m, int64_t d,
+                            int64_t ldw, int bits, float* scale, uint8_t* zero,
+                            hipStream_t st) {
+  const float maxq = static_cast<float>((1 << bits) - 1);
+  if (dt == GPTQ_F32)
+    fit_rows_kernel<float><<<static_cast<unsigned>(m), 64, 0, st>>>(
+        static_cast<const float*>(W), d, ldw, maxq, scale, zero);
+  else
+    fit_rows_kernel<uint16_t><<<static_cast<unsigned>(m), 64, 0, st>>>(
+        static_cast<const uint16_t*>(W), d, ldw, maxq, scale, zero);
+  GPTQ_CHECK_LAUNCH();
+  return GPTQ_OK;
+}
+
+gptq_status launch_init_work(const void* W, gptq_dtype dt, int64_t m,
+                             int64_t d, int64_t ldw, const int32_t* perm,
+                             const uint8_t* dead, float* WT, int32_t* pinv,
+                             hipStream_t st) {
+  pinv_kernel<<<cdiv(d, 256), 256, 0, st>>>(perm, d, pinv);
+  GPTQ_CHECK_LAUNCH();
+  const dim3 grid(cdiv(m, 64), cdiv(d, 64));
+  if (dt == GPTQ_F32)
+    init_work_kernel<float><<<grid, 256, 0, st>>>(static_cast<const float*>(W), m, d, ldw, perm, dead, WT);
+  else
+    init_work_kernel<uint16_t><<<grid, 256, 0, st>>>(static_cast<const uint16_t*>(W), m, d, ldw, perm, dead, WT);
+  GPTQ_CHECK_LAUNCH();
+  return GPTQ_OK;
+}
+
+gptq_status launch_rbt(const float* R, int64_t d, int bi, float* RbT,
+                       hipStream_t st) {
+  const int64_t nblk = (d + bi - 1) / bi;
+  rbt_kernel<<<dim3(cdiv(int64_t(bi) * bi, 256 * 8), static_cast<unsigned>(nblk)), 256, 0, st>>>(R, d, bi, RbT);
+  GPTQ_CHECK_LAUNCH();
+  return GPTQ_OK;
+}
+
+gptq_status launch_chain(float* WT, int64_t m, int64_t d, const float* R,
+                         const float* RbT, int64_t i0, int bw, int sb, int bi,
+                         int bits, int64_t gsize, float* scalesP,
+                         uint8_t* zerosP, uint8_t* codesP, float* E,
+                         hipStream_t st) {
+  const float maxq = static_cast<float>((1 << bits) - 1);
+  int fs = 0;
+  if (gsize > 0) {
+    fs = 1;
+    while (fs < kSB && gsize % (2 * fs) == 0) fs *= 2;
+  }
+  const dim3 grid(cdiv(m, 64));
+#define GPTQ_CHAIN(FSV)                                                        \
+  chain_kernel<FSV><<<grid, 64, 0, st>>>(WT, m, d, R, RbT, i0, bw, sb, bi,     \
+                                         maxq, gsize, scalesP, zerosP, codesP, E)
+  switch (fs) {
+    case 0: GPTQ_CHAIN(0); break;
+    case 1: GPTQ_CHAIN(1); break;
+    case 2: GPTQ_CHAIN(2); break;
+    case 4: GPTQ_CHAIN(4); break;
+    case 8: GPTQ_CHAIN(8); break;
+    case 16: GPTQ_CHAIN(16); break;
+    default: GPTQ_CHAIN(32); break;
+  }
+#undef GPTQ_CHAIN
+  GPTQ_CHECK_LAUNCH();
+  return GPTQ_OK;
+}
+
+gptq_status launch_lazy_update(float* WT, int64_t m, int64_t d, const float* R,
+                               int64_t i0, int bw, const float* E,
+                               hipStream_t st) {
+  const int64_t nT = d - i0 - bw;
+  if (nT <= 0) return GPTQ_OK;
+  lazy_update_kernel<<<dim3(cdiv(m, 128), cdiv(nT, 128)), 256, 0, st>>>(WT, m, d, R, i0, bw, E);
+  GPTQ_CHECK_LAUNCH();
+  return GPTQ_OK;
+}
+
+}  // namespace gptq
