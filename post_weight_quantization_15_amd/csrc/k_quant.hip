@@ -137,11 +137,12 @@ __global__ __launch_bounds__(64) void chain_kernel(
   const bool act = r < m;
   const int64_t rr = act ? r : 0;
   for (int c = 0; c < bw; ++c) rows[c][lane] = WT[(i0 + c) * m + rr];
-  float scale = 1.0f, zero = 0.0f;
-  if (FS == 0) {
-    scale = scalesP[rr];
-    zero = static_cast<float>(zerosP[rr]);
-  }
+  // grid in force at the block start: the row grid, or the dynamic group
+  // that contains column i0 (fitted by this launch if it starts here, by an
+  // earlier launch otherwise)
+  const int64_t g0 = (FS == 0) ? 0 : i0 / gsize;
+  float scale = scalesP[g0 * m + rr];
+  float zero = static_cast<float>(zerosP[g0 * m + rr]);
   for (int s0 = 0; s0 < bw; s0 += sb) {
     const int sw = min(sb, bw - s0);
     float w[kSB], eta[kSB];
