@@ -1,0 +1,180 @@
+"""Benchmark: one GPTQ linear layer end to end on one MI355X.
+
+Workload: the attention-projection layer -- W 4096 x 4096 bf16 ~ N(0, 0.02),
+262144 calibration tokens (128 x 2048) of low-rank + noise activations with
+1% outlier channels x20, 4-bit, group 128, block 128, percdamp 0.01.
+Synthetic, seeded; inputs are resident in HBM before timing starts.
+
+One step = the whole hot path: zero S, S += X^T X over all tokens, then
+quantize the layer (H, dead fix, damping, R = chol(H^-1) upper, column loop
+with lazy block updates, unpermute + pack), outputs in HBM.
+
+Prints one JSON line.  The `roofline` object covers the dominant kernel,
+timed live with HIP events on the stream the library launches on; the
+`cpu_baseline` object is the float64 oracle timed on a bounded sample of the
+same layer on the host cores.
+"""
+
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2500.0       # MI355X dense bf16 MFMA
+PEAK_HBM_GBS = 8000.0
+
+METRIC = "seconds per linear layer (4096x4096, 262144 tok, 4-bit g128); % MFMA/HBM peak"
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=5)
+    ap.add_argument("--warmup", type=int, default=2)
+    ap.add_argument("--tokens", type=int, default=128 * 2048)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-tokens", type=int, default=16384,
+                    help="token sample for the oracle's statistics")
+    ap.add_argument("--cpu-rows", type=int, default=256,
+                    help="row sample for the oracle's column loop")
+    return ap.parse_args()
+
+
+def kernel_source_hash(name):
+    with open(os.path.join(ROOT, "post_weight_quantization_15_amd", "csrc", name), "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def traffic_from_profile(src_hash, launches_per_step=1):
+    """HBM bytes per launch of the Hessian kernel from the committed counter
+    summary, if it was taken on the current kernel source."""
+    path = os.path.join(ROOT, "profiles", "hessian_attn_proj_traffic.json")
+    try:
+        with open(path) as f:
+            rec = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if rec.get("kernel_source_sha256_16") != src_hash:
+        return None
+    return rec.get("hbm_bytes_per_launch")
+
+
+def cpu_baseline(W, X, params, n_tokens, cpu_tokens, cpu_rows):
+    """The oracle as it stands, on a bounded sample, scaled to one layer."""
+    import numpy as np
+    import oracle as orc
+    try:
+        from threadpoolctl import threadpool_info
+        cores = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
+    except Exception:       # noqa: BLE001
+        cores = os.cpu_count()
+    m, d = W.shape
+    Xs = X[:cpu_tokens].float().cpu().numpy()
+    t0 = time.perf_counter()
+    S_part = orc.hessian_sum(Xs)
+    t_stats = (time.perf_counter() - t0) * (n_tokens / Xs.shape[0])
+    S = S_part * (n_tokens / Xs.shape[0])       # stand-in statistics for timing
+    t0 = time.perf_counter()
+    H, perm, dead, damp = orc.prepare(S, n_tokens, params["percdamp"], params["act_order"])
+    R, damp = orc.factor(H, damp)
+    t_factor = time.perf_counter() - t0
+    Wr = W[:cpu_rows].double().cpu().numpy()
+    t0 = time.perf_counter()
+    Wp = Wr.copy()
+    Wp[:, dead] = 0.0
+    Wp = Wp[:, perm]
+    out = orc.quantize_columns(Wp, R, params["bits"], params["group_size"],
+                               params["blocksize"],
+                               orc.fit_grid(Wr, params["bits"]) if params["group_size"] == -1 else None)
+    codes = np.empty_like(out["codes"])
+    codes[:, perm] = out["codes"]
+    orc.pack_codes(codes, params["bits"])
+    t_loop = (time.perf_counter() - t0) * (m / Wr.shape[0])
+    total = t_stats + t_factor + t_loop
+    return {"value": total, "unit": "s per layer", "cores": int(cores), "kind": "oracle",
+            "sample": (f"statistics on {Xs.shape[0]} of {n_tokens} tokens x{n_tokens / Xs.shape[0]:g}; "
+                       f"factor at full d={d}; column loop + packing on {Wr.shape[0]} of {m} rows "
+                       f"x{m / Wr.shape[0]:g}; phases s: stats {t_stats:.2f}, factor {t_factor:.2f}, "
+                       f"loop {t_loop:.2f}")}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); the layer "
+              "path has no multi-GPU mode in this build", file=sys.stderr)
+        sys.exit(2)
+    import torch
+    import post_weight_quantization_15_amd as gq
+    import synth
+
+    dev = torch.device("cuda:0")
+    gq.load_library()
+    L = synth.attn_proj_layer(dev, n=args.tokens)
+    W, X, params = L["W"], L["X"], L["params"]
+    m, d = W.shape
+    N = X.shape[0]
+    S = torch.zeros(d, d, dtype=torch.float32, device=dev)
+    hws = torch.empty(max(gq.gptq_hessian_workspace_bytes(d, N), 1), dtype=torch.uint8, device=dev)
+    qws = torch.empty(gq.gptq_workspace_bytes(m, d, **params), dtype=torch.uint8, device=dev)
+    torch.cuda.synchronize()
+
+    def step(ev=None):
+        S.zero_()
+        if ev:
+            ev[0].record()
+        gq.gptq_hessian_accumulate(S, X, ws=hws)
+        if ev:
+            ev[1].record()
+        out = gq.gptq_quantize_layer(W, S, N, ws=qws, **params)
+        if ev:
+            ev[2].record()
+        return out
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+    t0 = time.perf_counter()
+    for k in range(args.steps):
+        out = step(evs[k])
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    ms_step = elapsed * 1e3 / args.steps
+    hess_ms = sum(e[0].elapsed_time(e[1]) for e in evs) / args.steps
+    quant_ms = sum(e[1].elapsed_time(e[2]) for e in evs) / args.steps
+
+    flops = float(N) * d * (d + 1)                 # symmetric X^T X
+    achieved = flops / (hess_ms * 1e-3) / 1e12
+    traffic = traffic_from_profile(kernel_source_hash("k_hessian.hip"))
+    roofline = {"kernel": "gptq_hessian_accumulate (bf16 MFMA split-K + fixed-order reduce)",
+                "bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS,
+                "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
+                "traffic": traffic,
+                "algorithmic": f"N*d*(d+1) = {flops:.4e} flop per launch"}
+    line = {
+        "metric": METRIC, "value": round(ms_step / 1e3, 6), "unit": "s",
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 4), "higher_is_better": False,
+        "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": f"attention-projection layer {m}x{d}, {N} tokens, "
+                               f"{params['bits']}-bit g{params['group_size']}",
+                   "m": m, "d": d, "tokens": N, **params},
+        "phases_ms": {"hessian": round(hess_ms, 4), "quantize": round(quant_ms, 4)},
+        "roofline": roofline,
+    }
+    if not args.no_cpu_baseline:
+        line["cpu_baseline"] = cpu_baseline(W, X, params, N, args.cpu_tokens, args.cpu_rows)
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

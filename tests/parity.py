@@ -141,6 +141,19 @@ def compare_layer(res, W, S, n, gpu, params, check_w_hat=True):
         if rel.max(initial=0.0) > SCALE_RTOL:
             problems.append(f"scale rel err {rel.max()}")
     report["rows_diverged"] = int(np.sum(first < d))
+    # each row's first divergence must sit on a near-tie of the independent
+    # oracle: its pre-rounding value (code) or -lo/Delta (zero point) lies
+    # within BAND of a rounding boundary
+    bad_first = 0
+    for r in np.nonzero(first < d)[0]:
+        j = int(first[r])
+        near = tie_distance(res.v_perm[r, j]) < BAND
+        if g > 0 and j % g == 0:
+            near = near or tie_distance(res.zsrc_perm[r, j // g]) < BAND
+        bad_first += not near
+    report["bad_first_divergence"] = bad_first
+    if bad_first:
+        problems.append(f"{bad_first} first divergences are not near-ties of the oracle")
     Wp = np.array(W, dtype=np.float64)
     Wp[:, res.dead] = 0.0
     Wp = Wp[:, res.perm]
