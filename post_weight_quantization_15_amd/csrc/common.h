@@ -94,8 +94,8 @@ gptq_status launch_rbt(const float* R, int64_t d, int bi, float* RbT,
 // Block [i0, i0 + bw) of the column loop, in sub-blocks of sb <= 32 columns.
 // scalesP/zerosP are [n_g][m] (processing-group major); for group_size -1
 // row 0 holds the row grids.
-gptq_status launch_chain(float* WT, int64_t m, int64_t d, const float* R,
-                         const float* RbT, int64_t i0, int bw, int sb, int bi,
+gptq_status launch_chain(float* WT, int64_t m, int64_t d, const float* RbT,
+                         int64_t i0, int bw, int sb, int bi,
                          int bits, int64_t gsize, float* scalesP,
                          uint8_t* zerosP, uint8_t* codesP, float* E,
                          hipStream_t st);

@@ -239,7 +239,7 @@ gptq_status gptq_quantize_layer(const void* W, gptq_dtype w_dtype, int64_t m,
   if ((s = launch_rbt(Ru, d, bi, q.RbT, st)) != GPTQ_OK) return s;
   for (int64_t i0 = 0; i0 < d; i0 += bi) {
     const int bw = static_cast<int>(std::min<int64_t>(bi, d - i0));
-    if ((s = launch_chain(q.WT, m, d, Ru, q.RbT, i0, bw, sb, bi, p->bits, gsize,
+    if ((s = launch_chain(q.WT, m, d, q.RbT, i0, bw, sb, bi, p->bits, gsize,
                           q.scalesP, q.zerosP, q.codesP, q.E, st)) != GPTQ_OK)
       return s;
     if ((s = launch_lazy_update(q.WT, m, d, Ru, i0, bw, q.E, st)) != GPTQ_OK)

@@ -117,28 +117,34 @@ __global__ __launch_bounds__(256) void build_h_kernel(
 // Step 1 + 2: diagonal block factor (every workgroup, in LDS) + panel solve
 // ---------------------------------------------------------------------------
 
-// A_KK (nbk x nbk, upper) = U U^T with U upper, in place in Ad.
-__device__ void factor_diag_block(double (*Ad)[kNb + 1], int nbk, int* flag,
-                                  bool report) {
+// A_KK (nbk x nbk, upper triangle in Ad) = U U^T with U upper, in place.
+// Step c (from the last column down) eliminates column c from the leading
+// block with the unscaled column, A_ij -= A_ic A_jc / A_cc (i <= j < c);
+// column c is final after its step, so U is formed at the end:
+// U_cc = sqrt(A_cc), U_ic = A_ic / U_cc.  One barrier per column.
+__device__ void factor_diag_block(double (*Ad)[kNb + 1], double* piv, int nbk,
+                                  int* flag, bool report) {
+  static_assert(kNb == 64, "index split below assumes 64 columns");
   for (int c = nbk - 1; c >= 0; --c) {
+    double p = Ad[c][c];
+    const bool bad = !(p > 0.0);
+    if (bad) p = 1.0;
     if (threadIdx.x == 0) {
-      double p = Ad[c][c];
-      if (!(p > 0.0)) {
-        if (report) atomicOr(flag, 1);
-        p = 1.0;
-      }
-      Ad[c][c] = sqrt(p);
+      piv[c] = p;
+      if (bad && report) atomicOr(flag, 1);
     }
-    __syncthreads();
-    const double ucc = Ad[c][c];
-    for (int i = threadIdx.x; i < c; i += blockDim.x) Ad[i][c] /= ucc;
-    __syncthreads();
-    for (int e = threadIdx.x; e < c * c; e += blockDim.x) {
-      const int i = e / c, j = e % c;
-      if (i <= j) Ad[i][j] -= Ad[i][c] * Ad[j][c];
+    const double pinv = 1.0 / p;
+    for (int e = threadIdx.x; e < kNb * kNb; e += blockDim.x) {
+      const int i = e >> 6, j = e & 63;
+      if (i <= j && j < c) Ad[i][j] -= Ad[i][c] * Ad[j][c] * pinv;
     }
     __syncthreads();
   }
+  for (int e = threadIdx.x; e < kNb * kNb; e += blockDim.x) {
+    const int i = e >> 6, j = e & 63;
+    if (i <= j && j < nbk) Ad[i][j] = (i == j) ? sqrt(piv[i]) : Ad[i][j] / sqrt(piv[j]);
+  }
+  __syncthreads();
 }
 
 // Block K = [k0, k0 + nbk).  Workgroup w solves rows [256w, 256w + 256) of
@@ -147,16 +153,17 @@ __global__ __launch_bounds__(256) void chol_panel_kernel(
     double* __restrict__ H, int64_t d, int64_t k0, int nbk,
     int* __restrict__ flag) {
   __shared__ double Ad[kNb][kNb + 1];
+  __shared__ double piv[kNb];
   for (int e = threadIdx.x; e < kNb * kNb; e += 256) {
-    const int i = e / kNb, j = e % kNb;
+    const int i = e >> 6, j = e & 63;
     Ad[i][j] = (i < nbk && j < nbk && i <= j) ? H[(k0 + i) * d + k0 + j] : 0.0;
   }
   __syncthreads();
-  factor_diag_block(Ad, nbk, flag, blockIdx.x == 0);
+  factor_diag_block(Ad, piv, nbk, flag, blockIdx.x == 0);
   if (blockIdx.x == 0) {
-    for (int e = threadIdx.x; e < nbk * nbk; e += 256) {
-      const int i = e / nbk, j = e % nbk;
-      if (i <= j) H[(k0 + i) * d + k0 + j] = Ad[i][j];
+    for (int e = threadIdx.x; e < kNb * kNb; e += 256) {
+      const int i = e >> 6, j = e & 63;
+      if (i <= j && j < nbk) H[(k0 + i) * d + k0 + j] = Ad[i][j];
     }
   }
   const int64_t r = int64_t(blockIdx.x) * 256 + threadIdx.x;
@@ -254,7 +261,7 @@ __global__ __launch_bounds__(64) void trtri_diag_kernel(
   const int64_t k0 = int64_t(blockIdx.x) * kNb;
   const int nbk = static_cast<int>(min<int64_t>(kNb, d - k0));
   for (int e = threadIdx.x; e < kNb * kNb; e += 64) {
-    const int i = e / kNb, j = e % kNb;
+    const int i = e >> 6, j = e & 63;
     Ud[i][j] = (i < nbk && j < nbk && i <= j) ? U[(k0 + i) * d + k0 + j] : (i == j ? 1.0 : 0.0);
   }
   __syncthreads();

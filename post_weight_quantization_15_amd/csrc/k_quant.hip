@@ -27,6 +27,8 @@ namespace {
 
 constexpr int kB = 128;   // largest block handled by one chain launch
 constexpr int kSB = 32;   // sub-block held in registers
+constexpr int kCW = 4;    // waves per chain workgroup (64 rows each)
+constexpr int kRtPitch = kB + 4;   // LDS pitch of the R tile (16-byte rows)
 
 __device__ inline float to_f32(float x) { return x; }
 __device__ inline float to_f32(uint16_t x) { return __uint_as_float(uint32_t(x) << 16); }
@@ -115,95 +117,167 @@ __global__ __launch_bounds__(256) void rbt_kernel(const float* __restrict__ R,
   }
 }
 
-// One block [i0, i0 + bw) of the column loop for all rows, one thread per
-// output row.  The block is processed in sub-blocks of up to kSB columns held
-// in registers; the rest of the block sits in lane-private LDS slots and
-// receives each sub-block's feedback in one batch (the in-block step of the
-// column loop applied with lazy batching inside the block).  FS: a dynamic
-// group can only start at sub-block offsets that are multiples of FS (0 = the
-// whole-row grid, no refits).  Groups that start inside a sub-block end
-// inside it (checked on the host), so every fit sees fully compensated
-// columns.
-template <int FS>
-__global__ __launch_bounds__(64) void chain_kernel(
-    float* __restrict__ WT, int64_t m, int64_t d, const float* __restrict__ R,
-    const float* __restrict__ RbT, int64_t i0, int bw, int sb, int bi,
-    float maxq, int64_t gsize, float* __restrict__ scalesP,
+// The column chain over one sub-block [s0, s0 + sw) held in registers.
+// FULL: sw == kSB, so no per-column guards are needed.
+template <int FS, bool FULL>
+__device__ __forceinline__ void chain_sub(
+    float (*rows)[64], float (*rt)[kRtPitch], const float* __restrict__ WT,
+    int64_t m, int64_t d, int64_t i0, int s0, int sw, int bw, float maxq,
+    int64_t gsize, int lane, int64_t rr, int64_t r, bool store, float& scale,
+    float& zero, float& inv_scale, float* __restrict__ scalesP,
     uint8_t* __restrict__ zerosP, uint8_t* __restrict__ codesP,
-    float* __restrict__ E) {
+    float* __restrict__ E, float (&eta)[kSB]) {
+  float w[kSB], rinv[kSB];
+#pragma clang loop unroll(full)
+  for (int k = 0; k < kSB; ++k) {
+    const bool in = FULL || k < sw;
+    w[k] = in ? rows[s0 + k][lane] : 0.0f;
+    rinv[k] = in ? 1.0f / rt[s0 + k][s0 + k] : 0.0f;
+    eta[k] = 0.0f;
+  }
+#pragma clang loop unroll(full)
+  for (int k = 0; k < kSB; ++k) {
+    if (!FULL && k >= sw) break;
+    const int64_t col = i0 + s0 + k;
+    if (FS > 0 && (k % (FS > 0 ? FS : 1)) == 0 && (col % gsize) == 0) {
+      const int64_t gend = min(col + gsize, d);
+      float lo = 0.0f, hi = 0.0f;
+#pragma clang loop unroll(full)
+      for (int c = k; c < kSB; ++c)
+        if ((FULL || c < sw) && col - k + c < gend) {
+          lo = fminf(lo, w[c]);
+          hi = fmaxf(hi, w[c]);
+        }
+      for (int c = s0 + sw; c < bw && i0 + c < gend; ++c) {
+        const float x = rows[c][lane];
+        lo = fminf(lo, x);
+        hi = fmaxf(hi, x);
+      }
+      for (int64_t cc = i0 + bw; cc < gend; ++cc) {
+        const float x = WT[cc * m + rr];
+        lo = fminf(lo, x);
+        hi = fmaxf(hi, x);
+      }
+      fit_grid(lo, hi, maxq, scale, zero);
+      inv_scale = 1.0f / scale;
+      if (store) {
+        scalesP[(col / gsize) * m + r] = scale;
+        zerosP[(col / gsize) * m + r] = static_cast<uint8_t>(zero);
+      }
+    }
+    const float x = w[k];
+    const float c = fminf(fmaxf(rintf(x * inv_scale) + zero, 0.0f), maxq);
+    const float q = scale * (c - zero);
+    eta[k] = (x - q) * rinv[k];
+    if (store) {
+      codesP[col * m + r] = static_cast<uint8_t>(c);
+      E[(s0 + k) * m + r] = eta[k];
+    }
+    // columns past sw (ragged sub-block) are never read again
+#pragma clang loop unroll(full)
+    for (int k2 = k + 1; k2 < kSB; ++k2)
+      w[k2] = fmaf(-eta[k], rt[s0 + k2][s0 + k], w[k2]);
+  }
+}
+
+// One block [i0, i0 + bw) of the column loop.  A workgroup covers 64 output
+// rows with kCW waves.  The block is processed in sub-blocks of up to kSB
+// columns held in registers; every wave runs the same sub-block chain for
+// its 64 rows (identical inputs give identical results, so no cross-lane
+// exchange is needed) and the waves split the batched feedback of the
+// sub-block into the rest of the block, which lives in LDS.  This is the
+// in-block step of the column loop with lazy batching inside the block.
+// The block's R tile is staged transposed in LDS: rt[c][k] = R[i0+k][i0+c],
+// so every R read is a wave-uniform LDS broadcast.
+// FS: a dynamic group can only start at sub-block offsets that are
+// multiples of FS (0 = the whole-row grid, no refits).  Groups that start
+// inside a sub-block end inside it (checked on the host), so every fit sees
+// fully compensated columns.
+// Inside the chain the quotients w / Delta and rho / R_jj are products with
+// fp32 reciprocals; they differ from the IEEE quotients by at most an ulp,
+// which can only matter within 1e-6 of a rounding boundary.
+template <int FS>
+__global__ __launch_bounds__(64 * kCW) void chain_kernel(
+    float* __restrict__ WT, int64_t m, int64_t d, const float* __restrict__ RbT,
+    int64_t i0, int bw, int sb, int bi, float maxq, int64_t gsize,
+    float* __restrict__ scalesP, uint8_t* __restrict__ zerosP,
+    uint8_t* __restrict__ codesP, float* __restrict__ E) {
   __shared__ float rows[kB][64];
-  const int lane = threadIdx.x;
+  __shared__ __attribute__((aligned(16))) float rt[kB][kRtPitch];
+  const int lane = threadIdx.x & 63;
+  const int wq = threadIdx.x >> 6;
+  const bool lead = wq == 0;
   const int64_t r = int64_t(blockIdx.x) * 64 + lane;
   const bool act = r < m;
   const int64_t rr = act ? r : 0;
-  for (int c = 0; c < bw; ++c) rows[c][lane] = WT[(i0 + c) * m + rr];
+  // stage the transposed R tile and the block's columns of these rows
+  const float* rbt = RbT + (i0 / bi) * int64_t(bi) * bi;
+  {
+    // all loads of this thread are issued before the first LDS store
+    float tb[2 * (kB / kCW)];
+#pragma clang loop unroll(full)
+    for (int u = 0; u < kB / kCW; ++u)
+#pragma clang loop unroll(full)
+      for (int h = 0; h < 2; ++h) {
+        const int c = wq + kCW * u, k = 64 * h + lane;
+        tb[2 * u + h] = (c < bw && k < bw) ? rbt[int64_t(c) * bi + k] : 0.0f;
+      }
+#pragma clang loop unroll(full)
+    for (int u = 0; u < kB / kCW; ++u)
+#pragma clang loop unroll(full)
+      for (int h = 0; h < 2; ++h) {
+        const int c = wq + kCW * u, k = 64 * h + lane;
+        if (c < bw && k < bw) rt[c][k] = tb[2 * u + h];
+      }
+  }
+  {
+    float buf[kB / kCW];
+#pragma clang loop unroll(full)
+    for (int u = 0; u < kB / kCW; ++u) {
+      const int c = wq + kCW * u;
+      buf[u] = (c < bw) ? WT[(i0 + c) * m + rr] : 0.0f;
+    }
+#pragma clang loop unroll(full)
+    for (int u = 0; u < kB / kCW; ++u) {
+      const int c = wq + kCW * u;
+      if (c < bw) rows[c][lane] = buf[u];
+    }
+  }
+  __syncthreads();
   // grid in force at the block start: the row grid, or the dynamic group
   // that contains column i0 (fitted by this launch if it starts here, by an
   // earlier launch otherwise)
   const int64_t g0 = (FS == 0) ? 0 : i0 / gsize;
   float scale = scalesP[g0 * m + rr];
   float zero = static_cast<float>(zerosP[g0 * m + rr]);
+  float inv_scale = 1.0f / scale;
   for (int s0 = 0; s0 < bw; s0 += sb) {
     const int sw = min(sb, bw - s0);
-    float w[kSB], eta[kSB];
-#pragma unroll
-    for (int k = 0; k < kSB; ++k) {
-      w[k] = (k < sw) ? rows[s0 + k][lane] : 0.0f;
-      eta[k] = 0.0f;
-    }
-#pragma unroll
-    for (int k = 0; k < kSB; ++k) {
-      if (k < sw) {
-        const int64_t col = i0 + s0 + k;
-        if (FS > 0 && (k % (FS > 0 ? FS : 1)) == 0 && (col % gsize) == 0) {
-          const int64_t gend = min(col + gsize, d);
-          float lo = 0.0f, hi = 0.0f;
-#pragma unroll
-          for (int c = k; c < kSB; ++c)
-            if (c < sw && col - k + c < gend) {
-              lo = fminf(lo, w[c]);
-              hi = fmaxf(hi, w[c]);
-            }
-          for (int c = s0 + sw; c < bw && i0 + c < gend; ++c) {
-            const float x = rows[c][lane];
-            lo = fminf(lo, x);
-            hi = fmaxf(hi, x);
-          }
-          for (int64_t cc = i0 + bw; cc < gend; ++cc) {
-            const float x = WT[cc * m + rr];
-            lo = fminf(lo, x);
-            hi = fmaxf(hi, x);
-          }
-          fit_grid(lo, hi, maxq, scale, zero);
-          if (act) {
-            scalesP[(col / gsize) * m + r] = scale;
-            zerosP[(col / gsize) * m + r] = static_cast<uint8_t>(zero);
-          }
-        }
-        const float* Rj = R + col * d + (col - k);   // row col, from the sub-block start
-        const float x = w[k];
-        const float c = fminf(fmaxf(rintf(x / scale) + zero, 0.0f), maxq);
-        const float q = scale * (c - zero);
-        eta[k] = (x - q) / Rj[k];
-        if (act) {
-          codesP[col * m + r] = static_cast<uint8_t>(c);
-          E[(s0 + k) * m + r] = eta[k];
-        }
-#pragma unroll
-        for (int k2 = k + 1; k2 < kSB; ++k2)
-          if (k2 < sw) w[k2] = fmaf(-eta[k], Rj[k2], w[k2]);
+    float eta[kSB];
+    if (sw == kSB)
+      chain_sub<FS, true>(rows, rt, WT, m, d, i0, s0, kSB, bw, maxq, gsize, lane,
+                          rr, r, lead && act, scale, zero, inv_scale, scalesP,
+                          zerosP, codesP, E, eta);
+    else
+      chain_sub<FS, false>(rows, rt, WT, m, d, i0, s0, sw, bw, maxq, gsize, lane,
+                           rr, r, lead && act, scale, zero, inv_scale, scalesP,
+                           zerosP, codesP, E, eta);
+    // feedback of this sub-block into the rest of the block, split by wave
+    if (sw == kSB) {
+      for (int c = s0 + sw + wq; c < bw; c += kCW) {
+        float x = rows[c][lane];
+#pragma clang loop unroll(full)
+        for (int k = 0; k < kSB; ++k) x = fmaf(-eta[k], rt[c][s0 + k], x);
+        rows[c][lane] = x;
+      }
+    } else {
+      for (int c = s0 + sw + wq; c < bw; c += kCW) {
+        float x = rows[c][lane];
+        for (int k = 0; k < sw; ++k) x = fmaf(-eta[k], rt[c][s0 + k], x);
+        rows[c][lane] = x;
       }
     }
-    // feedback of this sub-block into the rest of the block
-    const float* rbt = RbT + (i0 / bi) * int64_t(bi) * bi;
-    for (int c = s0 + sw; c < bw; ++c) {
-      const float* rt = rbt + int64_t(c) * bi + s0;   // rt[k] = R[i0+s0+k][i0+c]
-      float x = rows[c][lane];
-#pragma unroll
-      for (int k = 0; k < kSB; ++k)
-        if (k < sw) x = fmaf(-eta[k], rt[k], x);
-      rows[c][lane] = x;
-    }
+    __syncthreads();
   }
 }
 
@@ -297,8 +371,8 @@ gptq_status launch_rbt(const float* R, int64_t d, int bi, float* RbT,
   return GPTQ_OK;
 }
 
-gptq_status launch_chain(float* WT, int64_t m, int64_t d, const float* R,
-                         const float* RbT, int64_t i0, int bw, int sb, int bi,
+gptq_status launch_chain(float* WT, int64_t m, int64_t d, const float* RbT,
+                         int64_t i0, int bw, int sb, int bi,
                          int bits, int64_t gsize, float* scalesP,
                          uint8_t* zerosP, uint8_t* codesP, float* E,
                          hipStream_t st) {
@@ -310,8 +384,9 @@ gptq_status launch_chain(float* WT, int64_t m, int64_t d, const float* R,
   }
   const dim3 grid(cdiv(m, 64));
 #define GPTQ_CHAIN(FSV)                                                        \
-  chain_kernel<FSV><<<grid, 64, 0, st>>>(WT, m, d, R, RbT, i0, bw, sb, bi,     \
-                                         maxq, gsize, scalesP, zerosP, codesP, E)
+  chain_kernel<FSV><<<grid, 64 * kCW, 0, st>>>(WT, m, d, RbT, i0, bw, sb, bi, \
+                                                maxq, gsize, scalesP, zerosP,  \
+                                                codesP, E)
   switch (fs) {
     case 0: GPTQ_CHAIN(0); break;
     case 1: GPTQ_CHAIN(1); break;
