@@ -13,14 +13,12 @@
 // chol_upper), with one factorisation instead of two.
 //
 // Blocked right-looking, from the last 64-column block to the first:
-//   1. factor the diagonal block A_KK = U_KK U_KK^T in LDS;
-//   2. panel: U_iK = A_iK U_KK^-T for every row i above the block;
+//   1. factor the diagonal block A_KK = U_KK U_KK^T and invert it,
+//      W_KK = U_KK^-1 (= R's diagonal block), in one workgroup;
+//   2. panel: U_iK = A_iK W_KK^T for every row i above the block (GEMM);
 //   3. trailing update A_ij -= U_iK U_jK^T (upper tiles only).
-// Steps 1-2 are one kernel: every workgroup refactors the 64x64 diagonal
-// block in LDS (cheap, avoids a launch) and then solves its own rows.
-// U_KK^-1 for every diagonal block is then formed in parallel, and the
-// off-diagonal blocks of R come from R_12 = -R_11 U_12 R_22 applied level by
-// level (block size 64, 128, 256, ...).
+// The off-diagonal blocks of R then come from R_12 = -R_11 U_12 R_22
+// applied level by level (block size 64, 128, 256, ...).
 #include <algorithm>
 #include <cmath>
 
@@ -114,111 +112,201 @@ __global__ __launch_bounds__(256) void build_h_kernel(
 }
 
 // ---------------------------------------------------------------------------
-// Step 1 + 2: diagonal block factor (every workgroup, in LDS) + panel solve
+// Step 1 + 2: diagonal block factor (every workgroup) + panel solve
 // ---------------------------------------------------------------------------
 
-// A_KK (nbk x nbk, upper triangle in Ad) = U U^T with U upper, in place.
-// Step c (from the last column down) eliminates column c from the leading
-// block with the unscaled column, A_ij -= A_ic A_jc / A_cc (i <= j < c);
-// column c is final after its step, so U is formed at the end:
-// U_cc = sqrt(A_cc), U_ic = A_ic / U_cc.  One barrier per column.
-__device__ void factor_diag_block(double (*Ad)[kNb + 1], double* piv, int nbk,
-                                  int* flag, bool report) {
-  static_assert(kNb == 64, "index split below assumes 64 columns");
+// Step 1 for the block K = [k0, k0 + nbk), nbk <= 64, one workgroup.
+//
+// A_KK = U_KK U_KK^T: thread t keeps the 16 elements (i = t/64 + 4u,
+// j = t%64), u = 0..15, of the block in registers for the whole
+// factorisation.  Column c is eliminated from the leading block with its
+// unscaled values, A_ij -= A_ic A_jc / A_cc (i <= j < c); the owners of
+// column c publish it through a double-buffered LDS vector, so each column
+// costs one barrier.  A column is final once its step has run, so U is
+// formed at the end: U_cc = sqrt(A_cc), U_ic = A_ic / U_cc.
+//
+// W_KK = U_KK^-1 by back substitution on rows with the same element split:
+// B = I; for i from the last row up, row i of W is B_i / U_ii and
+// B_k -= U_ki W_i for k < i.  W_KK is R's diagonal block (R = U^-1).
+__global__ __launch_bounds__(256) void chol_diag_kernel(
+    double* __restrict__ H, double* __restrict__ R, int64_t d, int64_t k0,
+    int nbk, int* __restrict__ flag) {
+  static_assert(kNb == 64, "thread/element split assumes 64 columns");
+  __shared__ double colbuf[2][kNb];
+  __shared__ double piv[kNb];
+  __shared__ double Ut[kNb][kNb + 1];   // Ut[c][i] = U[i][c]
+  const int wv = threadIdx.x >> 6, j = threadIdx.x & 63;
+  double a[16];
+#pragma unroll
+  for (int u = 0; u < 16; ++u) {
+    const int i = wv + 4 * u;
+    a[u] = (i <= j && j < nbk) ? H[(k0 + i) * d + k0 + j] : 0.0;
+  }
   for (int c = nbk - 1; c >= 0; --c) {
-    double p = Ad[c][c];
+    double* cb = colbuf[c & 1];
+    if (j == c) {
+#pragma unroll
+      for (int u = 0; u < 16; ++u) cb[wv + 4 * u] = a[u];
+    }
+    __syncthreads();
+    // all reads first, then branch-free masked updates: entries i > j of a
+    // thread are never published as valid data, entries of columns j >= c
+    // are final and must stay untouched
+    double ci[16];
+#pragma unroll
+    for (int u = 0; u < 16; ++u) ci[u] = cb[wv + 4 * u];
+    double p = cb[c];
+    const double cj = cb[j];
     const bool bad = !(p > 0.0);
     if (bad) p = 1.0;
     if (threadIdx.x == 0) {
       piv[c] = p;
-      if (bad && report) atomicOr(flag, 1);
+      if (bad) atomicOr(flag, 1);
     }
-    const double pinv = 1.0 / p;
-    for (int e = threadIdx.x; e < kNb * kNb; e += blockDim.x) {
-      const int i = e >> 6, j = e & 63;
-      if (i <= j && j < c) Ad[i][j] -= Ad[i][c] * Ad[j][c] * pinv;
+    const double sj = cj * (1.0 / p);      // A_jc / A_cc for this thread's column
+    const bool live = j < c;
+#pragma unroll
+    for (int u = 0; u < 16; ++u) {
+      const double nv = fma(-ci[u], sj, a[u]);
+      a[u] = live ? nv : a[u];
     }
-    __syncthreads();
-  }
-  for (int e = threadIdx.x; e < kNb * kNb; e += blockDim.x) {
-    const int i = e >> 6, j = e & 63;
-    if (i <= j && j < nbk) Ad[i][j] = (i == j) ? sqrt(piv[i]) : Ad[i][j] / sqrt(piv[j]);
   }
   __syncthreads();
-}
-
-// Block K = [k0, k0 + nbk).  Workgroup w solves rows [256w, 256w + 256) of
-// the panel: x U_KK^T = A_iK, in place, one row per thread.
-__global__ __launch_bounds__(256) void chol_panel_kernel(
-    double* __restrict__ H, int64_t d, int64_t k0, int nbk,
-    int* __restrict__ flag) {
-  __shared__ double Ad[kNb][kNb + 1];
-  __shared__ double piv[kNb];
-  for (int e = threadIdx.x; e < kNb * kNb; e += 256) {
-    const int i = e >> 6, j = e & 63;
-    Ad[i][j] = (i < nbk && j < nbk && i <= j) ? H[(k0 + i) * d + k0 + j] : 0.0;
+  {
+    const double rs = (j < nbk) ? 1.0 / sqrt(piv[j]) : 0.0;
+#pragma unroll
+    for (int u = 0; u < 16; ++u) {
+      const int i = wv + 4 * u;
+      double uval = 0.0;
+      if (j < nbk && i <= j) uval = (i == j) ? sqrt(piv[j]) : a[u] * rs;
+      Ut[j][i] = uval;
+      if (j < nbk && i <= j) H[(k0 + i) * d + k0 + j] = uval;
+    }
   }
   __syncthreads();
-  factor_diag_block(Ad, piv, nbk, flag, blockIdx.x == 0);
-  if (blockIdx.x == 0) {
-    for (int e = threadIdx.x; e < kNb * kNb; e += 256) {
-      const int i = e >> 6, j = e & 63;
-      if (i <= j && j < nbk) H[(k0 + i) * d + k0 + j] = Ad[i][j];
-    }
-  }
-  const int64_t r = int64_t(blockIdx.x) * 256 + threadIdx.x;
-  if (r >= k0) return;
-  double* row = H + r * d + k0;
-  double x[kNb];
+  // W = U^-1; b[u] holds B[k][j], k = wv + 4u
+  double b[16];
 #pragma unroll
-  for (int c = 0; c < kNb; ++c) x[c] = (c < nbk) ? row[c] : 0.0;
-  // x U^T = a  <=>  sum_{c' >= c} x[c'] U[c][c'] = a[c]; solve from the end
-#pragma unroll
-  for (int c = kNb - 1; c >= 0; --c) {
-    if (c < nbk) {
-      x[c] /= Ad[c][c];
-#pragma unroll
-      for (int c2 = 0; c2 < c; ++c2) x[c2] -= x[c] * Ad[c2][c];
-    }
-  }
-#pragma unroll
-  for (int c = 0; c < kNb; ++c)
-    if (c < nbk) row[c] = x[c];
-}
-
-// ---------------------------------------------------------------------------
-// fp64 tile GEMM core: 64x64 output tile, 256 threads x (4x4), k-step 16
-// ---------------------------------------------------------------------------
-
-template <class FA, class FB>
-__device__ inline void tile_gemm(int64_t kbeg, int64_t kend, FA fa, FB fb,
-                                 double acc[4][4]) {
-  __shared__ double As[16][68];
-  __shared__ double Bs[16][68];
-  const int tx = threadIdx.x & 15, ty = threadIdx.x >> 4;
-  for (int64_t k0 = kbeg; k0 < kend; k0 += 16) {
-    for (int e = threadIdx.x; e < 16 * 64; e += 256) {
-      const int kk = e >> 6, ii = e & 63;
-      const int64_t k = k0 + kk;
-      As[kk][ii] = k < kend ? fa(ii, k) : 0.0;
-      Bs[kk][ii] = k < kend ? fb(k, ii) : 0.0;
-    }
-    __syncthreads();
-#pragma unroll
-    for (int kk = 0; kk < 16; ++kk) {
-      double av[4], bv[4];
-#pragma unroll
-      for (int u = 0; u < 4; ++u) {
-        av[u] = As[kk][ty * 4 + u];
-        bv[u] = Bs[kk][tx * 4 + u];
+  for (int u = 0; u < 16; ++u) b[u] = (wv + 4 * u == j) ? 1.0 : 0.0;
+#pragma clang loop unroll(full)
+  for (int i = kNb - 1; i >= 0; --i) {
+    if (i < nbk) {
+      double* rb = colbuf[i & 1];
+      const double rinv = 1.0 / Ut[i][i];
+      if (wv == (i & 3)) {
+        b[i >> 2] *= rinv;
+        rb[j] = b[i >> 2];
       }
+      __syncthreads();
+      const double wij = rb[j];
+      double uk[16];
 #pragma unroll
-      for (int u = 0; u < 4; ++u)
+      for (int u = 0; u < 16; ++u) uk[u] = Ut[i][wv + 4 * u];
 #pragma unroll
-        for (int w = 0; w < 4; ++w) acc[u][w] = fma(av[u], bv[w], acc[u][w]);
+      for (int u = 0; u < 16; ++u) {
+        const double nv = fma(-uk[u], wij, b[u]);
+        b[u] = (wv + 4 * u < i) ? nv : b[u];
+      }
+    }
+  }
+#pragma unroll
+  for (int u = 0; u < 16; ++u) {
+    const int k = wv + 4 * u;
+    if (k < nbk && j < nbk) R[(k0 + k) * d + k0 + j] = (k <= j) ? b[u] : 0.0;
+  }
+}
+
+// ---------------------------------------------------------------------------
+// fp64 tile GEMM core on the matrix cores: a 64x64 output tile per 256-thread
+// workgroup, each wave a 32x32 quarter of 2x2 v_mfma_f64_16x16x4_f64 blocks.
+// Lane l feeds A[row = l%16][k = l/16] and B[k = l/16][col = l%16] and
+// receives D[row = l/16 + 4v][col = l%16] (the fp64 instruction interleaves
+// its output rows differently from the fp32 one).  K is staged through LDS in
+// chunks of 32 with the next chunk's loads issued before the current one is
+// consumed.  fa(i, k) / fb(k, j) return operand elements (0 outside);
+// B_KC: B's memory order has k contiguous (else j contiguous), which picks
+// the coalesced thread-to-element map for loading it.
+// ---------------------------------------------------------------------------
+
+typedef double f64x4 __attribute__((ext_vector_type(4)));
+constexpr int kKc = 32;            // k chunk
+constexpr int kLp = kKc + 2;       // LDS pitch (doubles)
+
+template <bool B_KC, class FA, class FB>
+__device__ inline void tile_gemm(int64_t kbeg, int64_t kend, FA fa, FB fb,
+                                 f64x4 acc[2][2]) {
+  __shared__ double As[64][kLp];
+  __shared__ double Bs[64][kLp];
+  const int t = threadIdx.x;
+  const int lane = t & 63, wv = t >> 6;
+  const int wr = (wv >> 1) * 32, wc = (wv & 1) * 32;
+  const int lr = lane & 15, lk = lane >> 4;
+  double ra[8], rb[8];
+  auto fetch = [&](int64_t k0) {
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const int e = t + 256 * u;
+      {
+        const int i = e >> 5, kk = e & 31;
+        const int64_t k = k0 + kk;
+        ra[u] = k < kend ? fa(i, k) : 0.0;
+      }
+      if (B_KC) {
+        const int j = e >> 5, kk = e & 31;
+        const int64_t k = k0 + kk;
+        rb[u] = k < kend ? fb(k, j) : 0.0;
+      } else {
+        const int kk = e >> 6, j = e & 63;
+        const int64_t k = k0 + kk;
+        rb[u] = k < kend ? fb(k, j) : 0.0;
+      }
+    }
+  };
+  if (kbeg < kend) fetch(kbeg);
+  for (int64_t k0 = kbeg; k0 < kend; k0 += kKc) {
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const int e = t + 256 * u;
+      As[e >> 5][e & 31] = ra[u];
+      if (B_KC)
+        Bs[e >> 5][e & 31] = rb[u];
+      else
+        Bs[e & 63][e >> 6] = rb[u];
+    }
+    __syncthreads();
+    if (k0 + kKc < kend) fetch(k0 + kKc);
+#pragma unroll
+    for (int ks = 0; ks < kKc; ks += 4) {
+      const double a0 = As[wr + lr][ks + lk], a1 = As[wr + 16 + lr][ks + lk];
+      const double b0 = Bs[wc + lr][ks + lk], b1 = Bs[wc + 16 + lr][ks + lk];
+      acc[0][0] = __builtin_amdgcn_mfma_f64_16x16x4f64(a0, b0, acc[0][0], 0, 0, 0);
+      acc[0][1] = __builtin_amdgcn_mfma_f64_16x16x4f64(a0, b1, acc[0][1], 0, 0, 0);
+      acc[1][0] = __builtin_amdgcn_mfma_f64_16x16x4f64(a1, b0, acc[1][0], 0, 0, 0);
+      acc[1][1] = __builtin_amdgcn_mfma_f64_16x16x4f64(a1, b1, acc[1][1], 0, 0, 0);
     }
     __syncthreads();
   }
+}
+
+// Output element (i, j) of the 64x64 tile held by this lane as acc[h][g][v].
+template <class F>
+__device__ inline void tile_store(const f64x4 acc[2][2], F f) {
+  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+  const int wr = (wv >> 1) * 32, wc = (wv & 1) * 32;
+#pragma unroll
+  for (int h = 0; h < 2; ++h)
+#pragma unroll
+    for (int g = 0; g < 2; ++g)
+#pragma unroll
+      for (int v = 0; v < 4; ++v)
+        f(wr + 16 * h + (lane >> 4) + 4 * v, wc + 16 * g + (lane & 15), acc[h][g][v]);
+}
+
+__device__ inline void zero_acc(f64x4 acc[2][2]) {
+#pragma unroll
+  for (int h = 0; h < 2; ++h)
+#pragma unroll
+    for (int g = 0; g < 2; ++g) acc[h][g] = f64x4{0.0, 0.0, 0.0, 0.0};
 }
 
 // Step 3: A[i][j] -= sum_c P[i][c] P[j][c] over the upper 64x64 tiles of
@@ -237,52 +325,41 @@ __global__ __launch_bounds__(256) void syrk_update_kernel(
     const int64_t j = J0 + jj;
     return j < k0 ? P[j * d + k] : 0.0;
   };
-  double acc[4][4] = {};
-  tile_gemm(0, nbk, fa, fb, acc);
-  const int tx = threadIdx.x & 15, ty = threadIdx.x >> 4;
-#pragma unroll
-  for (int u = 0; u < 4; ++u)
-#pragma unroll
-    for (int w = 0; w < 4; ++w) {
-      const int64_t i = I0 + ty * 4 + u, j = J0 + tx * 4 + w;
-      if (i < k0 && j < k0 && i <= j) H[i * d + j] -= acc[u][w];
-    }
+  f64x4 acc[2][2];
+  zero_acc(acc);
+  tile_gemm<true>(0, nbk, fa, fb, acc);
+  tile_store(acc, [&](int ii, int jj, double v) {
+    const int64_t i = I0 + ii, j = J0 + jj;
+    if (i < k0 && j < k0 && i <= j) H[i * d + j] -= v;
+  });
+}
+
+// Step 2: U_iK = A_iK W_KK^T for the rows i < k0, 64 rows per workgroup,
+// in place (a workgroup reads all of its rows' panel before writing it).
+__global__ __launch_bounds__(256) void chol_panel_kernel(
+    double* __restrict__ H, const double* __restrict__ R, int64_t d,
+    int64_t k0, int nbk) {
+  const int64_t I0 = int64_t(blockIdx.x) * 64;
+  const double* W = R + k0 * d + k0;
+  auto fa = [&](int ii, int64_t k) -> double {
+    const int64_t i = I0 + ii;
+    return i < k0 ? H[i * d + k0 + k] : 0.0;
+  };
+  auto fb = [&](int64_t k, int jj) -> double {   // B(k, j) = W[j][k], upper
+    return (jj < nbk && k >= jj) ? W[int64_t(jj) * d + k] : 0.0;
+  };
+  f64x4 acc[2][2];
+  zero_acc(acc);
+  tile_gemm<true>(0, nbk, fa, fb, acc);
+  tile_store(acc, [&](int ii, int jj, double v) {
+    const int64_t i = I0 + ii;
+    if (i < k0 && jj < nbk) H[i * d + k0 + jj] = v;
+  });
 }
 
 // ---------------------------------------------------------------------------
 // R = U^-1
 // ---------------------------------------------------------------------------
-
-// Each 64x64 diagonal block: R_KK = U_KK^-1 (upper).  Thread j solves
-// U x = e_j by back substitution for column j.
-__global__ __launch_bounds__(64) void trtri_diag_kernel(
-    const double* __restrict__ U, double* __restrict__ R, int64_t d) {
-  __shared__ double Ud[kNb][kNb + 1];
-  const int64_t k0 = int64_t(blockIdx.x) * kNb;
-  const int nbk = static_cast<int>(min<int64_t>(kNb, d - k0));
-  for (int e = threadIdx.x; e < kNb * kNb; e += 64) {
-    const int i = e >> 6, j = e & 63;
-    Ud[i][j] = (i < nbk && j < nbk && i <= j) ? U[(k0 + i) * d + k0 + j] : (i == j ? 1.0 : 0.0);
-  }
-  __syncthreads();
-  const int j = threadIdx.x;
-  double x[kNb];
-#pragma unroll
-  for (int i = 0; i < kNb; ++i) x[i] = (i == j) ? 1.0 : 0.0;
-#pragma unroll
-  for (int i = kNb - 1; i >= 0; --i) {
-    if (i <= j) {
-      x[i] /= Ud[i][i];
-#pragma unroll
-      for (int i2 = 0; i2 < i; ++i2) x[i2] -= Ud[i2][i] * x[i];
-    }
-  }
-  if (j < nbk) {
-#pragma unroll
-    for (int i = 0; i < kNb; ++i)
-      if (i < nbk) R[(k0 + i) * d + k0 + j] = (i <= j) ? x[i] : 0.0;
-  }
-}
 
 // Level s: pairs p of adjacent diagonal blocks I = [2ps, 2ps+s),
 // J = [2ps+s, min(2ps+2s, d)).  T_p = U_IJ R_JJ  (R_JJ upper: k <= j).
@@ -303,17 +380,14 @@ __global__ __launch_bounds__(256) void trtri_t_kernel(
     const int64_t j = j0 + jj;
     return (k <= j && j < sJ) ? R[(J0 + k) * d + J0 + j] : 0.0;
   };
-  double acc[4][4] = {};
-  tile_gemm(0, min<int64_t>(sJ, j0 + 64), fa, fb, acc);
+  f64x4 acc[2][2];
+  zero_acc(acc);
+  tile_gemm<false>(0, min<int64_t>(sJ, j0 + 64), fa, fb, acc);
   double* Tp = T + p * s * s;
-  const int tx = threadIdx.x & 15, ty = threadIdx.x >> 4;
-#pragma unroll
-  for (int u = 0; u < 4; ++u)
-#pragma unroll
-    for (int w = 0; w < 4; ++w) {
-      const int64_t i = i0 + ty * 4 + u, j = j0 + tx * 4 + w;
-      if (i < s && j < sJ) Tp[i * s + j] = acc[u][w];
-    }
+  tile_store(acc, [&](int ii, int jj, double v) {
+    const int64_t i = i0 + ii, j = j0 + jj;
+    if (i < s && j < sJ) Tp[i * s + j] = v;
+  });
 }
 
 // R_IJ = -R_II T_p  (R_II upper: k >= i).
@@ -336,16 +410,13 @@ __global__ __launch_bounds__(256) void trtri_r_kernel(
     const int64_t j = j0 + jj;
     return (j < sJ) ? Tp[k * s + j] : 0.0;
   };
-  double acc[4][4] = {};
-  tile_gemm(i0, s, fa, fb, acc);
-  const int tx = threadIdx.x & 15, ty = threadIdx.x >> 4;
-#pragma unroll
-  for (int u = 0; u < 4; ++u)
-#pragma unroll
-    for (int w = 0; w < 4; ++w) {
-      const int64_t i = i0 + ty * 4 + u, j = j0 + tx * 4 + w;
-      if (i < s && j < sJ) R[(I0 + i) * d + J0 + j] = -acc[u][w];
-    }
+  f64x4 acc[2][2];
+  zero_acc(acc);
+  tile_gemm<false>(i0, s, fa, fb, acc);
+  tile_store(acc, [&](int ii, int jj, double v) {
+    const int64_t i = i0 + ii, j = j0 + jj;
+    if (i < s && j < sJ) R[(I0 + i) * d + J0 + j] = -v;
+  });
 }
 
 __global__ __launch_bounds__(256) void r_to_f32_kernel(
@@ -420,9 +491,11 @@ gptq_status launch_cholesky_upper(int64_t d, const FactorWs& f,
   while (k1 > 0) {
     const int nbk = static_cast<int>((k1 % kNb) ? (k1 % kNb) : kNb);
     const int64_t k0 = k1 - nbk;
-    chol_panel_kernel<<<std::max(1u, cdiv(k0, 256)), 256, 0, st>>>(f.H, d, k0, nbk, f.flag);
+    chol_diag_kernel<<<1, 256, 0, st>>>(f.H, f.R, d, k0, nbk, f.flag);
     GPTQ_CHECK_LAUNCH();
     if (k0 > 0) {
+      chol_panel_kernel<<<cdiv(k0, 64), 256, 0, st>>>(f.H, f.R, d, k0, nbk);
+      GPTQ_CHECK_LAUNCH();
       const unsigned nt = cdiv(k0, 64);
       syrk_update_kernel<<<dim3(nt, nt), 256, 0, st>>>(f.H, d, k0, nbk);
       GPTQ_CHECK_LAUNCH();
@@ -434,10 +507,9 @@ gptq_status launch_cholesky_upper(int64_t d, const FactorWs& f,
 
 gptq_status launch_triangular_inverse(int64_t d, const FactorWs& f,
                                       hipStream_t st) {
-  // Diagonal blocks are aligned to multiples of 64 from the top; the
-  // Cholesky's block boundaries do not matter for the inverse.
-  trtri_diag_kernel<<<cdiv(d, kNb), 64, 0, st>>>(f.H, f.R, d);
-  GPTQ_CHECK_LAUNCH();
+  // The diagonal blocks of R (64-aligned from the top, the last one partial)
+  // were formed by the Cholesky's diagonal kernel; combine them level by
+  // level.
   for (int64_t s = kNb; s < d; s *= 2) {
     const unsigned pairs = cdiv(d, 2 * s);
     const dim3 grid(cdiv(s, 64), cdiv(s, 64), pairs);
