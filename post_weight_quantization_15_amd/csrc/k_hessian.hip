@@ -40,6 +40,50 @@ __device__ inline void tile_of(int64_t L, int nt, int& ti, int& tj) {
   tj = t + static_cast<int>(rem);
 }
 
+// XCD-aware work order.  Workgroup w runs on XCD w % 8, in dispatch order
+// within its XCD.  The upper tiles are enumerated block-major (blocks of
+// kRegB x kRegB tiles, row-major over the upper block triangle, row-major
+// inside a block) and cut into 8 consecutive regions, one per XCD; each XCD
+// walks its region split by split.  Concurrent waves of one XCD therefore
+// read the same token window of a compact set of panels, which its L2 can
+// serve, instead of every XCD streaming every panel.
+constexpr int kRegB = 8;
+constexpr int kXcd = 8;
+
+__device__ inline void blocked_tile(int64_t t, int nt, int& ti, int& tj) {
+  const int nb = (nt + kRegB - 1) / kRegB;
+  for (int br = 0; br < nb; ++br) {
+    const int r0 = br * kRegB, rh = min(kRegB, nt - r0);
+    for (int bc = br; bc < nb; ++bc) {
+      const int c0 = bc * kRegB, cw = min(kRegB, nt - c0);
+      const int64_t size = (bc == br) ? int64_t(rh) * (rh + 1) / 2 : int64_t(rh) * cw;
+      if (t >= size) {
+        t -= size;
+        continue;
+      }
+      if (bc == br) {
+        int i = 0;
+        while (t >= rh - i) {
+          t -= rh - i;
+          ++i;
+        }
+        ti = r0 + i;
+        tj = r0 + i + static_cast<int>(t);
+      } else {
+        ti = r0 + static_cast<int>(t / cw);
+        tj = c0 + static_cast<int>(t % cw);
+      }
+      return;
+    }
+  }
+  ti = tj = 0;
+}
+
+// Row-major index of upper tile (ti, tj) (the partial-sum layout).
+__device__ inline int64_t upper_index(int ti, int tj, int nt) {
+  return int64_t(ti) * nt - int64_t(ti) * (ti - 1) / 2 + (tj - ti);
+}
+
 // Lane (g = lane/16, fi = lane%16) covers tokens t0+8g .. t0+8g+7 and
 // features f .. f+7 of a panel (f = F0 + 8*fi); raw[q] holds token t0+8g+q.
 //
@@ -106,11 +150,18 @@ __global__ __launch_bounds__(64) void hessian_bf16_kernel(
     const uint16_t* __restrict__ X, int64_t ldx, int64_t n_tok, int64_t d,
     int nt, int64_t ks, int nsplit, float* __restrict__ S,
     float* __restrict__ part) {
-  const int64_t L = blockIdx.x;
-  const int split = blockIdx.y;
+  // work item of this workgroup (see blocked_tile)
+  const int64_t ntiles = upper_tiles(nt);
+  const int64_t per_xcd = (ntiles + kXcd - 1) / kXcd;
+  const int64_t w = blockIdx.x;
+  const int64_t pos = w / kXcd;
+  const int split = static_cast<int>(pos / per_xcd);
+  const int64_t t = (w % kXcd) * per_xcd + pos % per_xcd;
+  if (t >= ntiles || split >= nsplit) return;
   const int lane = threadIdx.x;
   int ti, tj;
-  tile_of(L, nt, ti, tj);
+  blocked_tile(t, nt, ti, tj);
+  const int64_t L = upper_index(ti, tj, nt);
   const int64_t F0 = int64_t(ti) * kTile, G0 = int64_t(tj) * kTile;
   const bool diag = ti == tj;
   const int64_t tbeg = int64_t(split) * ks;
@@ -342,7 +393,8 @@ gptq_status launch_hessian(float* S, int64_t d, const void* X, gptq_dtype dt,
   }
   const int nt = static_cast<int>((d + kTile - 1) / kTile);
   const SplitPlan p = plan_splits(d, n_tok);
-  hessian_bf16_kernel<<<dim3(static_cast<unsigned>(upper_tiles(nt)), p.nsplit), 64, 0, st>>>(
+  const int64_t per_xcd = (upper_tiles(nt) + kXcd - 1) / kXcd;
+  hessian_bf16_kernel<<<dim3(static_cast<unsigned>(kXcd * per_xcd * p.nsplit)), 64, 0, st>>>(
       static_cast<const uint16_t*>(X), ldx, n_tok, d, nt, p.ks, p.nsplit, S,
       static_cast<float*>(ws));
   GPTQ_CHECK_LAUNCH();
