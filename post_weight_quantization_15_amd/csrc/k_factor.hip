@@ -125,9 +125,10 @@ __global__ __launch_bounds__(256) void build_h_kernel(
 // costs one barrier.  A column is final once its step has run, so U is
 // formed at the end: U_cc = sqrt(A_cc), U_ic = A_ic / U_cc.
 //
-// W_KK = U_KK^-1 by back substitution on rows with the same element split:
-// B = I; for i from the last row up, row i of W is B_i / U_ii and
-// B_k -= U_ki W_i for k < i.  W_KK is R's diagonal block (R = U^-1).
+// W_KK = U_KK^-1 in log depth: the eight 8x8 diagonal blocks are inverted
+// in parallel, then neighbouring blocks are combined with
+// W_12 = -W_11 U_12 W_22 at sizes 8, 16, 32.  W_KK is R's diagonal block
+// (R = U^-1).
 __global__ __launch_bounds__(256) void chol_diag_kernel(
     double* __restrict__ H, double* __restrict__ R, int64_t d, int64_t k0,
     int nbk, int* __restrict__ flag) {
@@ -135,6 +136,8 @@ __global__ __launch_bounds__(256) void chol_diag_kernel(
   __shared__ double colbuf[2][kNb];
   __shared__ double piv[kNb];
   __shared__ double Ut[kNb][kNb + 1];   // Ut[c][i] = U[i][c]
+  __shared__ double Wt[kNb][kNb + 1];
+  __shared__ double Tl[kNb / 2][kNb / 2 + 1];
   const int wv = threadIdx.x >> 6, j = threadIdx.x & 63;
   double a[16];
 #pragma unroll
@@ -163,7 +166,11 @@ __global__ __launch_bounds__(256) void chol_diag_kernel(
       piv[c] = p;
       if (bad) atomicOr(flag, 1);
     }
-    const double sj = cj * (1.0 / p);      // A_jc / A_cc for this thread's column
+    // 1/p from the hardware reciprocal refined by two Newton steps
+    double rp = __builtin_amdgcn_rcp(p);
+    rp = rp * fma(-p, rp, 2.0);
+    rp = rp * fma(-p, rp, 2.0);
+    const double sj = cj * rp;             // A_jc / A_cc for this thread's column
     const bool live = j < c;
 #pragma unroll
     for (int u = 0; u < 16; ++u) {
@@ -184,35 +191,58 @@ __global__ __launch_bounds__(256) void chol_diag_kernel(
     }
   }
   __syncthreads();
-  // W = U^-1; b[u] holds B[k][j], k = wv + 4u
-  double b[16];
+  // W = U^-1 in log depth: invert the eight 8x8 diagonal blocks (one
+  // column per thread), then combine neighbours, W_12 = -W_11 U_12 W_22,
+  // for block sizes 8, 16, 32.
+  double (*Wl)[kNb + 1] = Wt;     // Wl[i][j] = W[i][j]
+  for (int e = threadIdx.x; e < kNb * kNb; e += 256) Wl[e >> 6][e & 63] = 0.0;
+  __syncthreads();
+  if (threadIdx.x < kNb) {
+    const int b = threadIdx.x >> 3, jj = threadIdx.x & 7, o = 8 * b;
+    double x[8];
 #pragma unroll
-  for (int u = 0; u < 16; ++u) b[u] = (wv + 4 * u == j) ? 1.0 : 0.0;
-#pragma clang loop unroll(full)
-  for (int i = kNb - 1; i >= 0; --i) {
-    if (i < nbk) {
-      double* rb = colbuf[i & 1];
-      const double rinv = 1.0 / Ut[i][i];
-      if (wv == (i & 3)) {
-        b[i >> 2] *= rinv;
-        rb[j] = b[i >> 2];
-      }
-      __syncthreads();
-      const double wij = rb[j];
-      double uk[16];
+    for (int i = 0; i < 8; ++i) x[i] = (i == jj) ? 1.0 : 0.0;
 #pragma unroll
-      for (int u = 0; u < 16; ++u) uk[u] = Ut[i][wv + 4 * u];
+    for (int i = 7; i >= 0; --i) {
+      if (i <= jj) {
+        double acc = x[i];
 #pragma unroll
-      for (int u = 0; u < 16; ++u) {
-        const double nv = fma(-uk[u], wij, b[u]);
-        b[u] = (wv + 4 * u < i) ? nv : b[u];
+        for (int k = i + 1; k < 8; ++k)
+          if (k <= jj) acc = fma(-Ut[o + k][o + i], x[k], acc);   // U[o+i][o+k]
+        x[i] = (o + i < nbk) ? acc / Ut[o + i][o + i] : 0.0;
       }
     }
-  }
 #pragma unroll
-  for (int u = 0; u < 16; ++u) {
-    const int k = wv + 4 * u;
-    if (k < nbk && j < nbk) R[(k0 + k) * d + k0 + j] = (k <= j) ? b[u] : 0.0;
+    for (int i = 0; i < 8; ++i)
+      if (i <= jj && o + jj < nbk) Wl[o + i][o + jj] = x[i];
+  }
+  __syncthreads();
+  for (int sz = 8; sz < kNb; sz *= 2) {
+    const int npair = kNb / (2 * sz);
+    // T_p[i][j] = sum_{k <= j} U[I0+i][J0+k] W[J0+k][J0+j]
+    for (int e = threadIdx.x; e < npair * sz * sz; e += 256) {
+      const int pr = e / (sz * sz), rem = e % (sz * sz);
+      const int i = rem / sz, jj = rem % sz;
+      const int I0 = 2 * pr * sz, J0 = I0 + sz;
+      double acc = 0.0;
+      for (int k = 0; k <= jj; ++k) acc = fma(Ut[J0 + k][I0 + i], Wl[J0 + k][J0 + jj], acc);
+      Tl[pr * sz + i][jj] = acc;
+    }
+    __syncthreads();
+    // W[I0+i][J0+j] = -sum_{k >= i} W[I0+i][I0+k] T_p[k][j]
+    for (int e = threadIdx.x; e < npair * sz * sz; e += 256) {
+      const int pr = e / (sz * sz), rem = e % (sz * sz);
+      const int i = rem / sz, jj = rem % sz;
+      const int I0 = 2 * pr * sz, J0 = I0 + sz;
+      double acc = 0.0;
+      for (int k = i; k < sz; ++k) acc = fma(Wl[I0 + i][I0 + k], Tl[pr * sz + k][jj], acc);
+      Wl[I0 + i][J0 + jj] = -acc;
+    }
+    __syncthreads();
+  }
+  for (int e = threadIdx.x; e < kNb * kNb; e += 256) {
+    const int k = e >> 6, jj = e & 63;
+    if (k < nbk && jj < nbk) R[(k0 + k) * d + k0 + jj] = (k <= jj) ? Wl[k][jj] : 0.0;
   }
 }
 
