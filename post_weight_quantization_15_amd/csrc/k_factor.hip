@@ -112,137 +112,168 @@ __global__ __launch_bounds__(256) void build_h_kernel(
 }
 
 // ---------------------------------------------------------------------------
-// Step 1 + 2: diagonal block factor (every workgroup) + panel solve
+// Step 1: diagonal block factor + inverse (one workgroup)
 // ---------------------------------------------------------------------------
 
-// Step 1 for the block K = [k0, k0 + nbk), nbk <= 64, one workgroup.
+typedef double f64x4 __attribute__((ext_vector_type(4)));
+
+__device__ inline double read_lane(double x, int l) {
+  const long long v = __double_as_longlong(x);
+  const int lo = __builtin_amdgcn_readlane(static_cast<int>(v), l);
+  const int hi = __builtin_amdgcn_readlane(static_cast<int>(v >> 32), l);
+  return __longlong_as_double((static_cast<long long>(hi) << 32) |
+                              static_cast<unsigned>(lo));
+}
+
+// 1/sqrt(p) from the hardware estimate and two Newton steps
+__device__ inline double rsqrt_refined(double p) {
+  double r = __builtin_amdgcn_rsq(p);
+  r = r * fma(-0.5 * p * r, r, 1.5);
+  r = r * fma(-0.5 * p * r, r, 1.5);
+  return r;
+}
+
+constexpr int kWp = kNb + 2;     // LDS pitch of the U / W arrays (16-B rows)
+
+// Step 1 for the block K = [k0, k0 + nbk), nbk <= 64, one 256-thread
+// workgroup; rows/columns past nbk are padded with the identity.
 //
-// A_KK = U_KK U_KK^T: thread t keeps the 16 elements (i = t/64 + 4u,
-// j = t%64), u = 0..15, of the block in registers for the whole
-// factorisation.  Column c is eliminated from the leading block with its
-// unscaled values, A_ij -= A_ic A_jc / A_cc (i <= j < c); the owners of
-// column c publish it through a double-buffered LDS vector, so each column
-// costs one barrier.  A column is final once its step has run, so U is
-// formed at the end: U_cc = sqrt(A_cc), U_ic = A_ic / U_cc.
+// A_KK = U_KK U_KK^T, four columns per barrier: thread (wave w, lane i)
+// holds A[i][j] for the columns j = w + 4u (u = 0..15), upper part i <= j.
+// For each group G = {g0..g0+3}, from the last one, the owners publish the
+// group's columns, every wave factors the 64 x 4 panel in registers (lane =
+// row; pivots from the right: U_cc = sqrt(A_cc), U_ic = A_ic / U_cc, then
+// the group's remaining columns lose U_:c U_c'c) and applies the rank-4
+// update A_ij -= sum_{c in G} U_ic U_jc to its columns j < g0.
 //
-// W_KK = U_KK^-1 in log depth: the eight 8x8 diagonal blocks are inverted
-// in parallel, then neighbouring blocks are combined with
-// W_12 = -W_11 U_12 W_22 at sizes 8, 16, 32.  W_KK is R's diagonal block
-// (R = U^-1).
+// W_KK = U_KK^-1 (R's diagonal block, R = U^-1): the four 16 x 16 diagonal
+// blocks by back substitution, then W_12 = -W_11 U_12 W_22 at sizes 16 and
+// 32 on the matrix cores.
 __global__ __launch_bounds__(256) void chol_diag_kernel(
     double* __restrict__ H, double* __restrict__ R, int64_t d, int64_t k0,
     int nbk, int* __restrict__ flag) {
   static_assert(kNb == 64, "thread/element split assumes 64 columns");
-  __shared__ double colbuf[2][kNb];
-  __shared__ double piv[kNb];
-  __shared__ double Ut[kNb][kNb + 1];   // Ut[c][i] = U[i][c]
-  __shared__ double Wt[kNb][kNb + 1];
-  __shared__ double Tl[kNb / 2][kNb / 2 + 1];
-  const int wv = threadIdx.x >> 6, j = threadIdx.x & 63;
+  __shared__ __align__(16) double Us[kNb][kWp];   // block staging, then U
+  __shared__ __align__(16) double Wl[kNb][kWp];   // W = U^-1
+  __shared__ double pan[2][4][kNb];
+  __shared__ double rsl[kNb];                     // 1 / U_cc
+  __shared__ __align__(16) double Tl[32][34];
+  const int t = threadIdx.x;
+  const int w = t >> 6, i = t & 63;
+  for (int e = t; e < kNb * kNb; e += 256) {
+    const int r = e >> 6, c = e & 63;
+    double v = (r == c) ? 1.0 : 0.0;
+    if (r < nbk && c < nbk && r <= c) v = H[(k0 + r) * d + k0 + c];
+    Us[r][c] = v;
+    Wl[r][c] = 0.0;
+  }
+  __syncthreads();
   double a[16];
 #pragma unroll
-  for (int u = 0; u < 16; ++u) {
-    const int i = wv + 4 * u;
-    a[u] = (i <= j && j < nbk) ? H[(k0 + i) * d + k0 + j] : 0.0;
-  }
-  for (int c = nbk - 1; c >= 0; --c) {
-    double* cb = colbuf[c & 1];
-    if (j == c) {
+  for (int u = 0; u < 16; ++u) a[u] = Us[i][w + 4 * u];
+  __syncthreads();
+  bool bad = false;
 #pragma unroll
-      for (int u = 0; u < 16; ++u) cb[wv + 4 * u] = a[u];
-    }
+  for (int g = 15; g >= 0; --g) {
+    const int g0 = 4 * g;
+    pan[g & 1][w][i] = a[g];             // column g0 + w
     __syncthreads();
-    // all reads first, then branch-free masked updates: entries i > j of a
-    // thread are never published as valid data, entries of columns j >= c
-    // are final and must stay untouched
-    double ci[16];
+    double P[4], Uc[4];
 #pragma unroll
-    for (int u = 0; u < 16; ++u) ci[u] = cb[wv + 4 * u];
-    double p = cb[c];
-    const double cj = cb[j];
-    const bool bad = !(p > 0.0);
-    if (bad) p = 1.0;
-    if (threadIdx.x == 0) {
-      piv[c] = p;
-      if (bad) atomicOr(flag, 1);
-    }
-    // 1/p from the hardware reciprocal refined by two Newton steps
-    double rp = __builtin_amdgcn_rcp(p);
-    rp = rp * fma(-p, rp, 2.0);
-    rp = rp * fma(-p, rp, 2.0);
-    const double sj = cj * rp;             // A_jc / A_cc for this thread's column
-    const bool live = j < c;
+    for (int cc = 0; cc < 4; ++cc) P[cc] = pan[g & 1][cc][i];
 #pragma unroll
-    for (int u = 0; u < 16; ++u) {
-      const double nv = fma(-ci[u], sj, a[u]);
-      a[u] = live ? nv : a[u];
+    for (int cc = 3; cc >= 0; --cc) {
+      const int c = g0 + cc;
+      double p = read_lane(P[cc], c);
+      const bool b = !(p > 0.0);
+      bad |= b;
+      p = b ? 1.0 : p;
+      const double rs = rsqrt_refined(p);
+      Uc[cc] = (i < c) ? P[cc] * rs : (i == c ? p * rs : 0.0);
+      if (t == 0) rsl[c] = rs;
+#pragma unroll
+      for (int c2 = cc - 1; c2 >= 0; --c2)
+        P[c2] = fma(-Uc[cc], read_lane(Uc[cc], g0 + c2), P[c2]);
     }
+    // every wave writes the same values; a wave reads back only after its
+    // own writes (LDS operations of one wave complete in order)
+    *reinterpret_cast<double2*>(&Us[i][g0]) = double2{Uc[0], Uc[1]};
+    *reinterpret_cast<double2*>(&Us[i][g0 + 2]) = double2{Uc[2], Uc[3]};
+    __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+#pragma unroll
+    for (int u = g - 1; u >= 0; --u) {   // the next group's column first
+      const int jr = w + 4 * u;
+      const double2 u01 = *reinterpret_cast<const double2*>(&Us[jr][g0]);
+      const double2 u23 = *reinterpret_cast<const double2*>(&Us[jr][g0 + 2]);
+      double v = a[u];
+      v = fma(-Uc[0], u01.x, v);
+      v = fma(-Uc[1], u01.y, v);
+      v = fma(-Uc[2], u23.x, v);
+      v = fma(-Uc[3], u23.y, v);
+      a[u] = v;
+    }
+  }
+  if (bad && t == 0) atomicOr(flag, 1);
+  __syncthreads();
+  const int lane = i, lr = lane & 15, lk = lane >> 4;
+  // 16 x 16 diagonal blocks of W: wave w, lanes 0..15 solve one column each
+  if (lane < 16) {
+    const int o = 16 * w, jj = lane;
+    double x[16];
+#pragma unroll
+    for (int ii = 15; ii >= 0; --ii) {
+      double acc = (ii == jj) ? 1.0 : 0.0;
+#pragma unroll
+      for (int k = ii + 1; k < 16; ++k) acc = fma(-Us[o + ii][o + k], x[k], acc);
+      x[ii] = acc * rsl[o + ii];
+    }
+#pragma unroll
+    for (int ii = 0; ii < 16; ++ii) Wl[o + ii][o + jj] = x[ii];
+  }
+  __syncthreads();
+  // size 16: pairs (0,1) and (2,3), one wave each
+  if (w < 2) {
+    const int A0 = 32 * w, B0 = A0 + 16;
+    f64x4 T = {0.0, 0.0, 0.0, 0.0}, Y = {0.0, 0.0, 0.0, 0.0};
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks)
+      T = __builtin_amdgcn_mfma_f64_16x16x4f64(Us[A0 + lr][B0 + 4 * ks + lk],
+                                                Wl[B0 + 4 * ks + lk][B0 + lr], T, 0, 0, 0);
+    // T's output row l/16 + 4v is the B operand row of k step v
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks)
+      Y = __builtin_amdgcn_mfma_f64_16x16x4f64(Wl[A0 + lr][A0 + 4 * ks + lk], T[ks], Y, 0, 0, 0);
+#pragma unroll
+    for (int v = 0; v < 4; ++v) Wl[A0 + lk + 4 * v][B0 + lr] = -Y[v];
+  }
+  __syncthreads();
+  // size 32: T = U_AB W_BB, then W_AB = -W_AA T; wave w owns tile (w/2, w%2)
+  {
+    const int r0 = 16 * (w >> 1), c0 = 16 * (w & 1);
+    f64x4 T = {0.0, 0.0, 0.0, 0.0};
+#pragma unroll
+    for (int ks = 0; ks < 8; ++ks)
+      T = __builtin_amdgcn_mfma_f64_16x16x4f64(Us[r0 + lr][32 + 4 * ks + lk],
+                                                Wl[32 + 4 * ks + lk][32 + c0 + lr], T, 0, 0, 0);
+#pragma unroll
+    for (int v = 0; v < 4; ++v) Tl[r0 + lk + 4 * v][c0 + lr] = T[v];
   }
   __syncthreads();
   {
-    const double rs = (j < nbk) ? 1.0 / sqrt(piv[j]) : 0.0;
+    const int r0 = 16 * (w >> 1), c0 = 16 * (w & 1);
+    f64x4 Y = {0.0, 0.0, 0.0, 0.0};
 #pragma unroll
-    for (int u = 0; u < 16; ++u) {
-      const int i = wv + 4 * u;
-      double uval = 0.0;
-      if (j < nbk && i <= j) uval = (i == j) ? sqrt(piv[j]) : a[u] * rs;
-      Ut[j][i] = uval;
-      if (j < nbk && i <= j) H[(k0 + i) * d + k0 + j] = uval;
-    }
+    for (int ks = 0; ks < 8; ++ks)
+      Y = __builtin_amdgcn_mfma_f64_16x16x4f64(Wl[r0 + lr][4 * ks + lk],
+                                                Tl[4 * ks + lk][c0 + lr], Y, 0, 0, 0);
+#pragma unroll
+    for (int v = 0; v < 4; ++v) Wl[r0 + lk + 4 * v][32 + c0 + lr] = -Y[v];
   }
   __syncthreads();
-  // W = U^-1 in log depth: invert the eight 8x8 diagonal blocks (one
-  // column per thread), then combine neighbours, W_12 = -W_11 U_12 W_22,
-  // for block sizes 8, 16, 32.
-  double (*Wl)[kNb + 1] = Wt;     // Wl[i][j] = W[i][j]
-  for (int e = threadIdx.x; e < kNb * kNb; e += 256) Wl[e >> 6][e & 63] = 0.0;
-  __syncthreads();
-  if (threadIdx.x < kNb) {
-    const int b = threadIdx.x >> 3, jj = threadIdx.x & 7, o = 8 * b;
-    double x[8];
-#pragma unroll
-    for (int i = 0; i < 8; ++i) x[i] = (i == jj) ? 1.0 : 0.0;
-#pragma unroll
-    for (int i = 7; i >= 0; --i) {
-      if (i <= jj) {
-        double acc = x[i];
-#pragma unroll
-        for (int k = i + 1; k < 8; ++k)
-          if (k <= jj) acc = fma(-Ut[o + k][o + i], x[k], acc);   // U[o+i][o+k]
-        x[i] = (o + i < nbk) ? acc / Ut[o + i][o + i] : 0.0;
-      }
-    }
-#pragma unroll
-    for (int i = 0; i < 8; ++i)
-      if (i <= jj && o + jj < nbk) Wl[o + i][o + jj] = x[i];
-  }
-  __syncthreads();
-  for (int sz = 8; sz < kNb; sz *= 2) {
-    const int npair = kNb / (2 * sz);
-    // T_p[i][j] = sum_{k <= j} U[I0+i][J0+k] W[J0+k][J0+j]
-    for (int e = threadIdx.x; e < npair * sz * sz; e += 256) {
-      const int pr = e / (sz * sz), rem = e % (sz * sz);
-      const int i = rem / sz, jj = rem % sz;
-      const int I0 = 2 * pr * sz, J0 = I0 + sz;
-      double acc = 0.0;
-      for (int k = 0; k <= jj; ++k) acc = fma(Ut[J0 + k][I0 + i], Wl[J0 + k][J0 + jj], acc);
-      Tl[pr * sz + i][jj] = acc;
-    }
-    __syncthreads();
-    // W[I0+i][J0+j] = -sum_{k >= i} W[I0+i][I0+k] T_p[k][j]
-    for (int e = threadIdx.x; e < npair * sz * sz; e += 256) {
-      const int pr = e / (sz * sz), rem = e % (sz * sz);
-      const int i = rem / sz, jj = rem % sz;
-      const int I0 = 2 * pr * sz, J0 = I0 + sz;
-      double acc = 0.0;
-      for (int k = i; k < sz; ++k) acc = fma(Wl[I0 + i][I0 + k], Tl[pr * sz + k][jj], acc);
-      Wl[I0 + i][J0 + jj] = -acc;
-    }
-    __syncthreads();
-  }
-  for (int e = threadIdx.x; e < kNb * kNb; e += 256) {
-    const int k = e >> 6, jj = e & 63;
-    if (k < nbk && jj < nbk) R[(k0 + k) * d + k0 + jj] = (k <= jj) ? Wl[k][jj] : 0.0;
+  for (int e = t; e < kNb * kNb; e += 256) {
+    const int r = e >> 6, c = e & 63;
+    if (r < nbk && c < nbk) R[(k0 + r) * d + k0 + c] = (r <= c) ? Wl[r][c] : 0.0;
   }
 }
 
@@ -258,7 +289,6 @@ __global__ __launch_bounds__(256) void chol_diag_kernel(
 // the coalesced thread-to-element map for loading it.
 // ---------------------------------------------------------------------------
 
-typedef double f64x4 __attribute__((ext_vector_type(4)));
 constexpr int kKc = 32;            // k chunk
 constexpr int kLp = kKc + 2;       // LDS pitch (doubles)
 

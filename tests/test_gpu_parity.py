@@ -116,7 +116,7 @@ def test_hessian_deterministic(dev):
 
 @pytest.mark.parametrize("d,act,dead_cols", [
     (1, False, ()), (65, False, ()), (200, True, ()), (300, False, (3, 77)),
-    (256, True, (0, 255)), (520, True, ()),
+    (256, True, (0, 255)), (520, True, ()), (1100, True, (5,)),
 ])
 def test_factor_matches_oracle(dev, d, act, dead_cols):
     n = 4 * d + 10
