@@ -100,7 +100,7 @@ gptq_status launch_chain(float* WT, int64_t m, int64_t d, const float* RbT,
                          uint8_t* zerosP, uint8_t* codesP, float* E,
                          hipStream_t st);
 gptq_status launch_lazy_update(float* WT, int64_t m, int64_t d, const float* R,
-                               int64_t i0, int bw, const float* E,
+                               int64_t i0, int bw, float* E,
                                hipStream_t st);
 gptq_status launch_outputs(int64_t m, int64_t d, int bits, int gsize,
                            const uint8_t* codesP, const float* scalesP,

@@ -281,53 +281,116 @@ __global__ __launch_bounds__(64 * kCW) void chain_kernel(
   }
 }
 
+__global__ void zero_fill_kernel(float* __restrict__ p, int64_t n) {
+  const int64_t i = int64_t(blockIdx.x) * blockDim.x + threadIdx.x;
+  if (i < n) p[i] = 0.0f;
+}
+
 // WT[i2 + t][r] -= sum_k R[i0 + k][i2 + t] * E[k][r]   (t < d - i2, r < m).
 // 256 threads = 2 x 2 waves, each a 64 (t) x 64 (r) tile of 4 x 4
-// 16x16 MFMA blocks.  Lane l feeds A[t = l%16][k = l/16] and
-// B[k = l/16][r = l%16]; it receives D[t = 4(l/16) + v][r = l%16].
-__global__ __launch_bounds__(256) void lazy_update_kernel(
+// 16x16x4 MFMA blocks.  Lane l feeds A[row = l%16][k = l/16] and
+// B[k = l/16][col = l%16] and receives D[row = 4(l/16) + v][col = l%16].
+// Block a of a wave covers t = tw + a + 4 row, block b covers
+// r = rw + b + 4 col, so a lane's four blocks touch four consecutive t (or r):
+// operands arrive as one 16-byte load per k step and the final
+// read-modify-write of W is one 16-byte access per (a, v).  Operands are
+// prefetched kDepth k steps ahead in a register ring; the W values to update
+// are loaded before the product starts.
+constexpr int kDepth = 4;
+
+// Elements c0..c0+3 of a row, the address clamped into [0, lim).  Lanes
+// whose columns fall past lim only feed outputs that are never stored, so
+// the data needs no masking (a select on loaded data would pin the wait for
+// the load next to the load).
+template <bool VEC>
+__device__ inline f32x4 load4(const float* row, int64_t c0, int64_t lim) {
+  if (VEC)     // lim, c0 multiples of 4 (lim >= 4), row 16-byte aligned
+    return *reinterpret_cast<const f32x4*>(row + (c0 < lim ? c0 : lim - 4));
+  f32x4 v;
+#pragma unroll
+  for (int c = 0; c < 4; ++c) v[c] = row[min(c0 + c, lim - 1)];
+  return v;
+}
+
+template <bool VEC, int KS>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2)))
+void lazy_update_kernel(
     float* __restrict__ WT, int64_t m, int64_t d, const float* __restrict__ R,
     int64_t i0, int bw, const float* __restrict__ E) {
   const int64_t i2 = i0 + bw, nT = d - i2;
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  const int64_t t0 = int64_t(blockIdx.y) * 128 + (wave >> 1) * 64;
-  const int64_t r0 = int64_t(blockIdx.x) * 128 + (wave & 1) * 64;
   const int lr = lane & 15, lk = lane >> 4;
+  const int64_t tw = int64_t(blockIdx.y) * 128 + (wave >> 1) * 64;
+  const int64_t rw = int64_t(blockIdx.x) * 128 + (wave & 1) * 64;
+  const int64_t ta = tw + 4 * lr, rb = rw + 4 * lr;
+  const float* Rt = R + i0 * d + i2;       // Rt[k d + t]
+  auto ldA = [&](int ks) -> f32x4 {
+    const int k = 4 * ks + lk;
+    return load4<VEC>(Rt + int64_t(min(k, bw - 1)) * d, ta, nT);
+  };
+  auto ldB = [&](int ks) -> f32x4 {
+    const int k = 4 * ks + lk;
+    return load4<VEC>(E + int64_t(k) * m, rb, m);     // rows >= bw are zero
+  };
+  f32x4 Wv[4][4];
+  auto ldW = [&]() {
+#pragma unroll
+    for (int a = 0; a < 4; ++a)
+#pragma unroll
+      for (int v = 0; v < 4; ++v) {
+        const int64_t t = tw + a + 16 * lk + 4 * v;
+        Wv[a][v] = load4<VEC>(WT + (i2 + min(t, nT - 1)) * m, rb, m);
+      }
+  };
+  constexpr int kWAt = KS > 8 ? KS - 8 : 0;   // step after which W is fetched
   f32x4 acc[4][4];
 #pragma unroll
   for (int a = 0; a < 4; ++a)
 #pragma unroll
     for (int b = 0; b < 4; ++b) acc[a][b] = f32x4{0.f, 0.f, 0.f, 0.f};
-  for (int k0 = 0; k0 < bw; k0 += 4) {
-    const int k = k0 + lk;
-    const bool kv = k < bw;
-    float av[4], bv[4];
+  // KS k steps (4 k each) cover bw, fully unrolled; rows bw..4 KS - 1 of E
+  // hold zeros, so the steps past bw add nothing.  Each step's MFMAs and the loads kDepth steps ahead are fenced
+  // from the scheduler so that the loads stay that far ahead of their use.
+  f32x4 A[kDepth], B[kDepth];
 #pragma unroll
-    for (int a = 0; a < 4; ++a) {
-      const int64_t t = t0 + 16 * a + lr;
-      av[a] = (kv && t < nT) ? R[(i0 + k) * d + i2 + t] : 0.0f;
-    }
+  for (int s = 0; s < kDepth && s < KS; ++s) {
+    A[s] = ldA(s);
+    B[s] = ldB(s);
+  }
+  __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-    for (int b = 0; b < 4; ++b) {
-      const int64_t rr = r0 + 16 * b + lr;
-      bv[b] = (kv && rr < m) ? E[int64_t(k) * m + rr] : 0.0f;
-    }
+  for (int ks = 0; ks < KS; ++ks) {
+    const int s = ks % kDepth;
 #pragma unroll
     for (int a = 0; a < 4; ++a)
 #pragma unroll
       for (int b = 0; b < 4; ++b)
-        acc[a][b] = __builtin_amdgcn_mfma_f32_16x16x4f32(av[a], bv[b], acc[a][b], 0, 0, 0);
+        acc[a][b] = __builtin_amdgcn_mfma_f32_16x16x4f32(A[s][a], B[s][b], acc[a][b], 0, 0, 0);
+    if (ks + kDepth < KS) {
+      A[s] = ldA(ks + kDepth);
+      B[s] = ldB(ks + kDepth);
+    }
+    if (ks == kWAt) ldW();
+    __builtin_amdgcn_sched_barrier(0);
   }
 #pragma unroll
   for (int a = 0; a < 4; ++a)
 #pragma unroll
-    for (int b = 0; b < 4; ++b)
+    for (int v = 0; v < 4; ++v) {
+      const int64_t t = tw + a + 16 * lk + 4 * v;
+      if (t >= nT) continue;
+      f32x4 x = Wv[a][v];
 #pragma unroll
-      for (int v = 0; v < 4; ++v) {
-        const int64_t t = t0 + 16 * a + 4 * lk + v;
-        const int64_t rr = r0 + 16 * b + lr;
-        if (t < nT && rr < m) WT[(i2 + t) * m + rr] -= acc[a][b][v];
+      for (int b = 0; b < 4; ++b) x[b] -= acc[a][b][v];
+      float* row = WT + (i2 + t) * m;
+      if (VEC) {
+        if (rb < m) *reinterpret_cast<f32x4*>(row + rb) = x;
+      } else {
+#pragma unroll
+        for (int b = 0; b < 4; ++b)
+          if (rb + b < m) row[rb + b] = x[b];
       }
+    }
 }
 
 unsigned cdiv(int64_t a, int64_t b) { return static_cast<unsigned>((a + b - 1) / b); }
@@ -402,11 +465,35 @@ gptq_status launch_chain(float* WT, int64_t m, int64_t d, const float* RbT,
 }
 
 gptq_status launch_lazy_update(float* WT, int64_t m, int64_t d, const float* R,
-                               int64_t i0, int bw, const float* E,
+                               int64_t i0, int bw, float* E,
                                hipStream_t st) {
   const int64_t nT = d - i0 - bw;
   if (nT <= 0) return GPTQ_OK;
-  lazy_update_kernel<<<dim3(cdiv(m, 128), cdiv(nT, 128)), 256, 0, st>>>(WT, m, d, R, i0, bw, E);
+  const dim3 grid(cdiv(m, 128), cdiv(nT, 128));
+  // 16-byte accesses need every row start and column offset 4-aligned
+  const bool vec = m % 4 == 0 && d % 4 == 0 && (i0 + bw) % 4 == 0 &&
+                   reinterpret_cast<uintptr_t>(R) % 16 == 0 &&
+                   reinterpret_cast<uintptr_t>(WT) % 16 == 0 &&
+                   reinterpret_cast<uintptr_t>(E) % 16 == 0;
+  const int ks = (bw + 3) / 4;      // k steps; bw <= 128
+  const int kpad = ks <= 4 ? 16 : ks <= 8 ? 32 : ks <= 16 ? 64 : 128;
+  if (kpad > bw) {     // rows of E the product reads past bw must be zero
+    const int64_t n = int64_t(kpad - bw) * m;
+    zero_fill_kernel<<<cdiv(n, 256), 256, 0, st>>>(E + int64_t(bw) * m, n);
+  }
+#define GPTQ_LAZY(V, K) lazy_update_kernel<V, K><<<grid, 256, 0, st>>>(WT, m, d, R, i0, bw, E)
+#define GPTQ_LAZY_KS(V)                        \
+  if (ks <= 4) GPTQ_LAZY(V, 4);                 \
+  else if (ks <= 8) GPTQ_LAZY(V, 8);            \
+  else if (ks <= 16) GPTQ_LAZY(V, 16);          \
+  else GPTQ_LAZY(V, 32);
+  if (vec) {
+    GPTQ_LAZY_KS(true)
+  } else {
+    GPTQ_LAZY_KS(false)
+  }
+#undef GPTQ_LAZY_KS
+#undef GPTQ_LAZY
   GPTQ_CHECK_LAUNCH();
   return GPTQ_OK;
 }
