@@ -44,6 +44,11 @@ def parse():
                     help="token sample for the oracle's statistics")
     ap.add_argument("--cpu-rows", type=int, default=256,
                     help="row sample for the oracle's column loop")
+    ap.add_argument("--phase", choices=("layer", "hessian"), default="layer",
+                    help="'hessian' times only the statistics call (for counter passes)")
+    ap.add_argument("--copy-probe-mib", type=int, default=0,
+                    help="after timing, run one device-to-device copy of this many MiB "
+                         "(a plain copy kernel of known size for scaling HBM counters)")
     return ap.parse_args()
 
 
@@ -133,7 +138,9 @@ def main():
         gq.gptq_hessian_accumulate(S, X, ws=hws)
         if ev:
             ev[1].record()
-        out = gq.gptq_quantize_layer(W, S, N, ws=qws, **params)
+        out = None
+        if args.phase == "layer":
+            out = gq.gptq_quantize_layer(W, S, N, ws=qws, **params)
         if ev:
             ev[2].record()
         return out
@@ -147,6 +154,14 @@ def main():
         out = step(evs[k])
     torch.cuda.synchronize()
     elapsed = time.perf_counter() - t0
+    if args.copy_probe_mib > 0:
+        nb = args.copy_probe_mib << 20
+        src = torch.ones(nb, dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
     ms_step = elapsed * 1e3 / args.steps
     hess_ms = sum(e[0].elapsed_time(e[1]) for e in evs) / args.steps
     quant_ms = sum(e[1].elapsed_time(e[2]) for e in evs) / args.steps
@@ -166,7 +181,8 @@ def main():
         "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
         "data": "synthetic",
         "config": {"workload": f"attention-projection layer {m}x{d}, {N} tokens, "
-                               f"{params['bits']}-bit g{params['group_size']}",
+                               f"{params['bits']}-bit g{params['group_size']}"
+                               + ("" if args.phase == "layer" else " (statistics only)"),
                    "m": m, "d": d, "tokens": N, **params},
         "phases_ms": {"hessian": round(hess_ms, 4), "quantize": round(quant_ms, 4)},
         "roofline": roofline,
