@@ -2,18 +2,26 @@
 //
 // [derivation] eq. (9): H = (2/N) X X^T with X = reshape(A, [N, d])^T
 // (eq. (5)); the sum is additive over calibration chunks (section 9.4).
+// The statistic is symmetric, so only the upper triangle is computed and
+// the result is mirrored.
 //
-// bf16 path (the hot path): one wave64 per (128x128 upper-triangle tile of S,
-// token split).  The contraction runs over tokens, the strided dimension of
-// the token-major input, so each lane gathers an 8-token x 8-feature block
-// with eight 16-byte loads and transposes it in registers into eight
-// 8-token fragments, one per feature.  A lane group (lane / 16) owns 8 tokens
-// of a 32-token step and lane % 16 selects 8 features, so fragment f of all
-// lanes is the A (or B) operand of one v_mfma_f32_16x16x32_bf16 whose
-// 16 rows are the features F0 + 8*i + f, i = 0..15.  8 x 8 such MFMAs cover
-// the 128 x 128 tile; no LDS is used.  bf16 x bf16 products are exact in
-// fp32 and accumulate in fp32.  Token splits write fp32 partial tiles that a
-// second kernel adds to S in a fixed order (bitwise reproducible).
+// bf16 path (the hot path): one workgroup of four wave64s per (256x256 upper
+// super-tile of S, token split); wave w owns the 128x128 sub-tile
+// (w / 2, w % 2) and its 256 fp32 accumulators fill the AGPR file.  The two
+// 256-feature panels of each 32-token step are staged once per workgroup in
+// LDS and shared by the four waves, which halves the L1/L2 traffic per MFMA
+// against waves that load their own operands.
+//  * Unmasked items: global_load_lds_dwordx4 copies the token rows straight
+//    into a four-stage LDS ring (loads run three steps ahead, no VGPRs), and
+//    ds_read_b64_tr_b16 transposes them into v_mfma_f32_16x16x32_bf16
+//    operands on the way out.
+//  * Masked items (a panel crossing d, a ragged last split): each thread
+//    gathers an 8-token x 8-feature block with 16-byte loads, zeroes what
+//    lies outside, transposes it in registers (v_perm_b32) and writes it
+//    feature-major into a double-buffered LDS stage.
+// bf16 x bf16 products are exact in fp32 and accumulate in fp32.  Token
+// splits write fp32 partial tiles that a second kernel adds to S in split
+// order with an fp64 running sum (bitwise reproducible).
 //
 // fp32 path: plain tiled kernel accumulating in fp64 (small inputs).
 #include <algorithm>
@@ -23,9 +31,16 @@
 namespace gptq {
 namespace {
 
-constexpr int kTile = 128;
-constexpr int kStep = 32;
-constexpr int kTargetWaves = 1024;   // 256 CUs x 4 SIMDs, one wave per SIMD
+constexpr int kSup = 256;                      // super-tile edge (features)
+constexpr int kStep = 32;                      // tokens per step
+constexpr int kThreads = 256;                  // four wave64s
+constexpr int kPanelBytes = 4 * kSup * 16;     // 4 token chunks x 256 features x 16 B
+constexpr int kStageBytes = 2 * kPanelBytes;
+constexpr int kLdsBytes = 2 * kStageBytes;     // two stages: 64 KiB
+constexpr int kSubElems = 128 * 128;           // one wave's partial tile
+constexpr int kCUs = 256;                      // MI355X compute units
+constexpr int kXcd = 8;                        // accelerator dies, own L2 each
+constexpr int kRegB = 4;                       // XCD regions: blocks of 4x4 super-tiles
 
 __host__ __device__ inline int64_t upper_tiles(int64_t nt) { return nt * (nt + 1) / 2; }
 
@@ -41,15 +56,11 @@ __device__ inline void tile_of(int64_t L, int nt, int& ti, int& tj) {
 }
 
 // XCD-aware work order.  Workgroup w runs on XCD w % 8, in dispatch order
-// within its XCD.  The upper tiles are enumerated block-major (blocks of
-// kRegB x kRegB tiles, row-major over the upper block triangle, row-major
-// inside a block) and cut into 8 consecutive regions, one per XCD; each XCD
-// walks its region split by split.  Concurrent waves of one XCD therefore
-// read the same token window of a compact set of panels, which its L2 can
-// serve, instead of every XCD streaming every panel.
-constexpr int kRegB = 8;
-constexpr int kXcd = 8;
-
+// within its XCD.  The upper super-tiles are enumerated block-major (blocks
+// of kRegB x kRegB, row-major over the upper block triangle, row-major inside
+// a block) and cut into 8 consecutive regions, one per XCD; each XCD walks
+// its region split by split.  Concurrent workgroups of one XCD therefore read
+// the same token window of a compact set of panels, which its L2 serves.
 __device__ inline void blocked_tile(int64_t t, int nt, int& ti, int& tj) {
   const int nb = (nt + kRegB - 1) / kRegB;
   for (int br = 0; br < nb; ++br) {
@@ -79,38 +90,27 @@ __device__ inline void blocked_tile(int64_t t, int nt, int& ti, int& tj) {
   ti = tj = 0;
 }
 
-// Row-major index of upper tile (ti, tj) (the partial-sum layout).
+// Row-major index of upper super-tile (ti, tj) (the partial-sum layout).
 __device__ inline int64_t upper_index(int ti, int tj, int nt) {
   return int64_t(ti) * nt - int64_t(ti) * (ti - 1) / 2 + (tj - ti);
 }
 
-// Lane (g = lane/16, fi = lane%16) covers tokens t0+8g .. t0+8g+7 and
-// features f .. f+7 of a panel (f = F0 + 8*fi); raw[q] holds token t0+8g+q.
+// Loader geometry of the masked path: thread t fetches panel t / 128 (0:
+// rows F0.., 1: columns G0..), features 8*fg .. 8*fg+7 with fg = t % 32,
+// tokens 8*tg .. 8*tg+7 of the step with tg = (t / 32) % 4; raw[q] holds
+// token 8*tg + q.
 //
-// Full steps: `base` = X + t0*ldx is wave-uniform and off[q] is the lane's
-// 32-bit element offset, so the loads take the scalar-base form and a step
-// only advances the base.
-__device__ inline void load_full(const uint16_t* __restrict__ base,
-                                 const uint32_t off[8], u32x4 raw[8]) {
-#pragma unroll
-  for (int q = 0; q < 8; ++q)
-    raw[q] = *reinterpret_cast<const u32x4*>(base + off[q]);
-}
-
 // Ragged steps (token tail, or a panel crossing d; needs d % 8 == 0 so a
-// lane's 8 features are all in range or all out): out-of-range rows and
+// lane's 8 features are all in range or all out): out-of-range tokens and
 // features read a clamped in-range address and are zeroed.
 __device__ inline void load_masked(const uint16_t* __restrict__ X, int64_t ldx,
-                                   int64_t t0, int64_t tlim, int64_t F0,
-                                   int64_t d, u32x4 raw[8]) {
-  const int lane = threadIdx.x;
-  const int64_t tb = t0 + 8 * (lane >> 4);
-  const int64_t f = F0 + 8 * (lane & 15);
+                                   int64_t tb, int64_t t0, int64_t tend,
+                                   int64_t f, int64_t d, u32x4 raw[8]) {
   const bool fv = f < d;
   const int64_t fc = fv ? f : 0;
 #pragma unroll
   for (int q = 0; q < 8; ++q) {
-    const bool tv = tb + q < tlim;
+    const bool tv = tb + q < tend;
     const u32x4 v = *reinterpret_cast<const u32x4*>(X + (tv ? tb + q : t0) * ldx + fc);
     raw[q] = (fv && tv) ? v : u32x4{0u, 0u, 0u, 0u};
   }
@@ -132,24 +132,241 @@ __device__ inline void transpose8x8(const u32x4 raw[8], u32x4 frag[8]) {
   }
 }
 
-__device__ inline bf16x8 as_bf16x8(u32x4 v) { return __builtin_bit_cast(bf16x8, v); }
-
-// 8 x 8 MFMAs: acc[a][b] += (features F0+8i+a) x (features G0+8j+b) over
-// the 32 tokens held in the fragments.
-__device__ inline void mfma_tile(const u32x4 fa[8], const u32x4 fb[8],
-                                 f32x4 acc[8][8]) {
-#pragma unroll
-  for (int a = 0; a < 8; ++a)
-#pragma unroll
-    for (int b = 0; b < 8; ++b)
-      acc[a][b] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
-          as_bf16x8(fa[a]), as_bf16x8(fb[b]), acc[a][b], 0, 0, 0);
+// LDS layout of one panel in one stage: 16-byte units (token chunk c = 0..3,
+// feature r = 0..255) at unit index c * 256 + (r ^ ((r >> 3) & 15)).  The XOR
+// keeps both access patterns free of bank conflicts: the loader's writes
+// (rows 8*fg + f for 16 consecutive fg) and the MFMA reads (16 consecutive
+// rows of one chunk) each touch 16 distinct 16-byte bank groups.
+__device__ inline uint32_t lds_unit(int c, int r) {
+  return static_cast<uint32_t>((c * kSup + (r ^ ((r >> 3) & 15))) * 16);
 }
 
-__global__ __launch_bounds__(64) void hessian_bf16_kernel(
+__device__ inline void store_panel(char* lds, uint32_t panel_off, int fg, int tg,
+                                   const u32x4 raw[8]) {
+  u32x4 frag[8];
+  transpose8x8(raw, frag);
+#pragma unroll
+  for (int f = 0; f < 8; ++f)
+    *reinterpret_cast<u32x4*>(lds + panel_off + lds_unit(tg, 8 * fg + f)) = frag[f];
+}
+
+__device__ inline bf16x8 as_bf16x8(u32x4 v) { return __builtin_bit_cast(bf16x8, v); }
+
+// Workgroup barrier between LDS stages.  Only LDS traffic is waited for: the
+// global loads of the steps ahead stay in flight across it.
+__device__ inline void stage_barrier() {
+  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
+
+// acc += A B on v_mfma_f32_16x16x32_bf16 with the accumulator pinned to the
+// AGPR file.  The 256 accumulator registers of a 128x128 sub-tile fill the
+// AGPRs exactly; left to itself the register allocator shuttles them between
+// the two files (and to scratch) once the staging registers are counted.
+// Consecutive MFMAs of a step use distinct accumulators; after the last
+// step acc_settle() covers the wait states before the results are read.
+__device__ inline void mfma_acc(f32x4& acc, const u32x4& a, const u32x4& b) {
+  asm volatile("v_mfma_f32_16x16x32_bf16 %0, %1, %2, %0" : "+a"(acc) : "v"(a), "v"(b));
+}
+
+__device__ inline void acc_settle() {
+  asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" ::: "memory");
+}
+
+// One 32-token step of a wave: 8 + 8 fragment reads, 8 x 8 MFMAs.
+// acc[a][b] lane l element v = sum over the step's tokens of
+// x[row 16a + 4(l/16) + v] * x[col 16b + l%16] within the wave's sub-tile.
+// The B fragments and the first two A fragments are read up front; A
+// fragment a + 2 is read while the MFMAs of row block a run.
+__device__ inline void mma_step(const char* lds, uint32_t a_off, uint32_t b_off,
+                                const uint32_t offA[8], const uint32_t offB[8],
+                                f32x4 acc[8][8]) {
+  u32x4 fa[8], fb[8];
+#pragma unroll
+  for (int b = 0; b < 8; ++b)
+    fb[b] = *reinterpret_cast<const u32x4*>(lds + b_off + offB[b]);
+  fa[0] = *reinterpret_cast<const u32x4*>(lds + a_off + offA[0]);
+  fa[1] = *reinterpret_cast<const u32x4*>(lds + a_off + offA[1]);
+#pragma unroll
+  for (int a = 0; a < 8; ++a) {
+    if (a + 2 < 8) fa[a + 2] = *reinterpret_cast<const u32x4*>(lds + a_off + offA[a + 2]);
+#pragma unroll
+    for (int b = 0; b < 8; ++b) {
+      mfma_acc(acc[a][b], fa[a], fb[b]);
+    }
+  }
+}
+
+// The step loop of a masked work item (a panel crossing d, or a ragged last
+// split): register-staged loads with zeros outside the data, the step count
+// padded to even with all-zero steps; loads of the steps past the end
+// re-read the last step.
+__device__ inline void run_masked(char* lds, const uint16_t* __restrict__ X,
+                                 int64_t ldx, int64_t d, int64_t tbeg,
+                                 int64_t tend, int64_t P0, uint32_t b_panel, const uint32_t offA[8],
+                                 const uint32_t offB[8], f32x4 acc[8][8]) {
+  const int tid = threadIdx.x;
+  const int lp = tid >> 7, fg = tid & 31, tg = (tid >> 5) & 3;
+  const uint32_t panel_off = static_cast<uint32_t>(lp) * kPanelBytes;
+  const int64_t nst = (tend - tbeg + kStep - 1) / kStep;
+  const int64_t nst2 = (nst + 1) & ~int64_t(1);
+  auto load_step = [&](int64_t s, u32x4 raw[8]) {
+    s = s < nst2 ? s : nst2 - 1;
+    const int64_t t0 = tbeg + s * kStep;
+    load_masked(X, ldx, t0 + 8 * tg, tbeg, tend, P0 + 8 * fg, d, raw);
+  };
+  // LDS stage k % 2 holds step k; raw0 / raw1 carry the loads of the even /
+  // odd step ahead, two steps before their use.
+  u32x4 raw0[8], raw1[8];
+  load_step(0, raw0);
+  load_step(1, raw1);
+  store_panel(lds, panel_off, fg, tg, raw0);
+  stage_barrier();
+  for (int64_t s = 0; s < nst2; s += 2) {
+    load_step(s + 2, raw0);
+    mma_step(lds, 0, b_panel, offA, offB, acc);
+    store_panel(lds, kStageBytes + panel_off, fg, tg, raw1);
+    stage_barrier();
+    load_step(s + 3, raw1);
+    mma_step(lds, kStageBytes, kStageBytes + b_panel, offA, offB, acc);
+    store_panel(lds, panel_off, fg, tg, raw0);
+    stage_barrier();
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Unmasked items: direct-to-LDS staging.  Each step's two panels (32 token
+// rows x 256 features each) go from global memory straight into LDS with
+// global_load_lds_dwordx4 (no VGPRs, no transposes), token-major, in a ring
+// of kStages stages, so the loads run kStages - 1 steps ahead of the MFMAs.
+// The MFMA operands are read with ds_read_b64_tr_b16, which transposes
+// within 16-lane groups: lane i of a group receives element i % 4 of the
+// 8-byte reads of lanes 4e + i / 4 (e = 0..3).  A lane group that points
+// lanes 4e + m at token row R + e, features F + 4m .. F + 4m + 3 thus gives
+// lane i the features F + i of tokens R .. R + 3 -- half an MFMA fragment.
+// ---------------------------------------------------------------------------
+constexpr int kStages = 4;
+constexpr int kRowBytes = kSup * 2;                    // one token row of a panel
+constexpr int kDmaPanel = kStep * kRowBytes;           // 16 KiB
+constexpr int kDmaStage = 2 * kDmaPanel;               // 32 KiB
+
+// 16-byte chunk c of token row r is stored at chunk c ^ swz(r).  Each
+// ds_read_b64_tr_b16 reads, per half-wave, 32 bytes from each of 8 rows
+// whose swz values differ in bits 1-3, so the 8 reads cover the 64 banks
+// once.
+__device__ inline int swz(int r) { return 2 * ((r & 3) | (((r >> 3) & 1) << 2)); }
+
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef const void __attribute__((address_space(1)))* gvoid;
+typedef void __attribute__((address_space(3)))* lvoid;
+
+__device__ inline uint2 tr_read(const char* lds, uint32_t off) {
+  const s16x4 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+      (__attribute__((address_space(3))) s16x4*)(lds + off));
+  return __builtin_bit_cast(uint2, v);
+}
+
+// Fragment: tokens 8*kg + e (from h = 0) and 8*kg + 4 + e (h = 1, four rows
+// = 2048 bytes further) of feature column `off` addresses.
+__device__ inline u32x4 tr_frag(const char* lds, uint32_t off) {
+  const uint2 lo = tr_read(lds, off), hi = tr_read(lds, off + 4 * kRowBytes);
+  return u32x4{lo.x, lo.y, hi.x, hi.y};
+}
+
+template <int n>
+__device__ inline void wait_vmcnt_le() {
+  // s_waitcnt with vmcnt = n (split field), expcnt and lgkmcnt at maximum
+  __builtin_amdgcn_s_waitcnt((n & 15) | ((n >> 4) << 14) | (7 << 4) | (15 << 8));
+}
+
+__device__ inline void run_dma(char* lds, const uint16_t* __restrict__ X,
+                               int64_t ldx, int64_t tbeg, int64_t nst,
+                               int64_t F0, int64_t G0, f32x4 acc[8][8]) {
+  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+  // loader role: wave wv fills panel wv / 2, rows 16 (wv % 2) + 2 i + lane / 32
+  // (instruction i = 0..7); lanes write 16 contiguous bytes each
+  const int p = wv >> 1;
+  const int64_t P0 = p ? G0 : F0;
+  uint32_t goff[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const int r = 16 * (wv & 1) + 2 * i + (lane >> 5);
+    const int c = (lane & 31) ^ swz(r);
+    goff[i] = static_cast<uint32_t>(2 * (r * ldx + P0 + 8 * c));
+  }
+  const uint32_t lds_row0 = static_cast<uint32_t>(p * kDmaPanel + 16 * (wv & 1) * kRowBytes);
+  // MFMA role: sub-tile (wa, wb); lane (kg, j) points at row 8 kg + j / 4,
+  // features 4 (j % 4) .. + 3 of each 16-feature block
+  const int wa = wv >> 1, wb = wv & 1;
+  const int kg = lane >> 4, j = lane & 15;
+  const int r0 = 8 * kg + (j >> 2);
+  const int sw = swz(r0);
+  uint32_t aoff[8], boff[8];
+#pragma unroll
+  for (int a = 0; a < 8; ++a) {
+    const int cl = 2 * a + ((j & 3) >> 1);
+    aoff[a] = static_cast<uint32_t>(r0 * kRowBytes + 16 * ((16 * wa + cl) ^ sw) + 8 * (j & 1));
+    boff[a] = static_cast<uint32_t>(kDmaPanel + r0 * kRowBytes + 16 * ((16 * wb + cl) ^ sw) + 8 * (j & 1));
+  }
+
+  // load i of step k (token rows 2i, 2i + 1 of this wave's half panel)
+  auto src_of = [&](int64_t k) {
+    const int64_t kk = k < nst ? k : nst - 1;
+    const uint16_t* base = X + (tbeg + kk * kStep) * ldx;
+    asm volatile("" : "+s"(base));
+    return reinterpret_cast<const char*>(base);
+  };
+  auto dst_of = [&](int64_t k) {
+    return lds + static_cast<uint32_t>(k % kStages) * kDmaStage + lds_row0;
+  };
+
+#pragma unroll
+  for (int k = 0; k < kStages - 1; ++k) {
+    const char* gb = src_of(k);
+    char* dst = dst_of(k);
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+      __builtin_amdgcn_global_load_lds((gvoid)(gb + goff[i]), (lvoid)(dst + 2 * i * kRowBytes),
+                                       16, 0, 0);
+  }
+  wait_vmcnt_le<8 * (kStages - 2)>();
+  stage_barrier();
+  for (int64_t s = 0; s < nst; ++s) {
+    // the loads of step s + kStages - 1 go out one per row block, between
+    // the MFMAs, so the address unit never holds up the MFMA issue
+    const char* gb = src_of(s + kStages - 1);
+    char* dst = dst_of(s + kStages - 1);
+    const char* st = lds + static_cast<uint32_t>(s % kStages) * kDmaStage;
+    u32x4 fa[8], fb[8];
+#pragma unroll
+    for (int b = 0; b < 8; ++b) fb[b] = tr_frag(st, boff[b]);
+    fa[0] = tr_frag(st, aoff[0]);
+    fa[1] = tr_frag(st, aoff[1]);
+#pragma unroll
+    for (int a = 0; a < 8; ++a) {
+#pragma unroll
+      for (int b = 0; b < 8; ++b) {
+        mfma_acc(acc[a][b], fa[a], fb[b]);
+        if (b == 1)
+          __builtin_amdgcn_global_load_lds((gvoid)(gb + goff[a]), (lvoid)(dst + 2 * a * kRowBytes),
+                                           16, 0, 0);
+        if (b == 3 && a + 2 < 8) fa[a + 2] = tr_frag(st, aoff[a + 2]);
+      }
+    }
+    wait_vmcnt_le<8 * (kStages - 2)>();
+    stage_barrier();
+  }
+}
+
+// kFull selects the work items this instance runs: the unmasked ones (both
+// panels inside [0, d), an even number of full steps) or the rest; the host
+// launches the masked instance only when such items exist.  Separate
+// instances keep the masked loop's registers out of the hot loop.
+template <bool kFull>
+__global__ __launch_bounds__(kThreads) void hessian_bf16_kernel(
     const uint16_t* __restrict__ X, int64_t ldx, int64_t n_tok, int64_t d,
     int nt, int64_t ks, int nsplit, float* __restrict__ S,
     float* __restrict__ part) {
+  __shared__ __attribute__((aligned(16))) char lds[kFull ? kStages * kDmaStage : kLdsBytes];
   // work item of this workgroup (see blocked_tile)
   const int64_t ntiles = upper_tiles(nt);
   const int64_t per_xcd = (ntiles + kXcd - 1) / kXcd;
@@ -158,15 +375,34 @@ __global__ __launch_bounds__(64) void hessian_bf16_kernel(
   const int split = static_cast<int>(pos / per_xcd);
   const int64_t t = (w % kXcd) * per_xcd + pos % per_xcd;
   if (t >= ntiles || split >= nsplit) return;
-  const int lane = threadIdx.x;
   int ti, tj;
   blocked_tile(t, nt, ti, tj);
-  const int64_t L = upper_index(ti, tj, nt);
-  const int64_t F0 = int64_t(ti) * kTile, G0 = int64_t(tj) * kTile;
   const bool diag = ti == tj;
+  const int64_t F0 = int64_t(ti) * kSup, G0 = int64_t(tj) * kSup;
   const int64_t tbeg = int64_t(split) * ks;
   const int64_t tend = min(tbeg + ks, n_tok);
-  const bool panels_full = (F0 + kTile <= d) && (G0 + kTile <= d);
+  const int64_t ntok = tend - tbeg;
+  const bool full = (F0 + kSup <= d) && (G0 + kSup <= d) && ntok % kStep == 0;
+  if (full != kFull) return;
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63, wv = tid >> 6;
+  // Loader role: threads 0-127 stage the row panel, 128-255 the column panel
+  // (on a diagonal super-tile both hold the same features).
+  const int64_t P0 = (tid >> 7) ? G0 : F0;
+  // MFMA role: wave wv owns sub-tile (wa, wb).  On a diagonal super-tile the
+  // lower sub-tile (1, 0) mirrors (0, 1): it is computed (keeping the step
+  // free of branches) but not written.
+  const int wa = wv >> 1, wb = wv & 1;
+  const bool busy = !(diag && wv == 2);
+  const int c = lane >> 4, i16 = lane & 15;
+  uint32_t offA[8], offB[8];
+#pragma unroll
+  for (int a = 0; a < 8; ++a) {
+    offA[a] = lds_unit(c, 128 * wa + 16 * a + i16);
+    offB[a] = lds_unit(c, 128 * wb + 16 * a + i16);
+  }
+  const uint32_t b_panel = static_cast<uint32_t>(kPanelBytes);
 
   f32x4 acc[8][8];
 #pragma unroll
@@ -174,102 +410,86 @@ __global__ __launch_bounds__(64) void hessian_bf16_kernel(
 #pragma unroll
     for (int b = 0; b < 8; ++b) acc[a][b] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  u32x4 ra[8], rb[8], fa[8], fb[8];
-  // full 32-token steps with both panels inside [0, d)
-  const int64_t nfull = panels_full ? (tend - tbeg) / kStep : 0;
-  if (nfull > 0) {
-    uint32_t offa[8], offb[8];
-    const int g8 = 8 * (lane >> 4), f8 = 8 * (lane & 15);
-#pragma unroll
-    for (int q = 0; q < 8; ++q) {
-      offa[q] = static_cast<uint32_t>((g8 + q) * ldx + F0 + f8);
-      offb[q] = static_cast<uint32_t>((g8 + q) * ldx + G0 + f8);
-    }
-    const uint16_t* base = X + tbeg * ldx;
-    const int64_t step = kStep * ldx;
-    // The fragments are loop-carried; the raw loads of step s+1 are issued
-    // before the MFMAs of step s and transposed after them.
-    load_full(base, offa, ra);
-    load_full(base, offb, rb);
-    transpose8x8(ra, fa);
-    transpose8x8(rb, fb);
-    for (int64_t s = 0; s < nfull; ++s) {
-      const bool more = s + 1 < nfull;
-      if (more) {
-        base += step;
-        load_full(base, offa, ra);
-        load_full(base, offb, rb);
-      }
-      mfma_tile(fa, fb, acc);
-      if (more) {
-        transpose8x8(ra, fa);
-        transpose8x8(rb, fb);
-      }
-    }
-  }
-  // ragged remainder (token tail of the split, or panels crossing d)
-  for (int64_t t0 = tbeg + nfull * kStep; t0 < tend; t0 += kStep) {
-    load_masked(X, ldx, t0, tend, F0, d, ra);
-    load_masked(X, ldx, t0, tend, G0, d, rb);
-    transpose8x8(ra, fa);
-    transpose8x8(rb, fb);
-    mfma_tile(fa, fb, acc);
-  }
+  if (kFull)
+    run_dma(lds, X, ldx, tbeg, ntok / kStep, F0, G0, acc);
+  else
+    run_masked(lds, X, ldx, d, tbeg, tend, P0, b_panel, offA, offB, acc);
+  acc_settle();
+  if (!busy) return;
 
-  // acc[f][f'][v] = S(F0 + 8*(4g+v) + f, G0 + 8*fi + f')
-  const int g = lane >> 4, fi = lane & 15;
   if (nsplit == 1) {
+    // acc[a][b][v] = S(F0 + 128wa + 16a + 4g + v, G0 + 128wb + 16b + i16)
+    const int g = lane >> 4;
 #pragma unroll
-    for (int v = 0; v < 4; ++v)
+    for (int a = 0; a < 8; ++a)
 #pragma unroll
-      for (int f = 0; f < 8; ++f) {
-        const int a = 8 * (4 * g + v) + f;
-        const int64_t i = F0 + a;
+      for (int v = 0; v < 4; ++v) {
+        const int64_t i = F0 + 128 * wa + 16 * a + 4 * g + v;
 #pragma unroll
-        for (int f2 = 0; f2 < 8; ++f2) {
-          const int b = 8 * fi + f2;
-          const int64_t j = G0 + b;
-          if (i < d && j < d && (!diag || a <= b)) {
-            const float nv = S[i * d + j] + acc[f][f2][v];
+        for (int b = 0; b < 8; ++b) {
+          const int64_t j = G0 + 128 * wb + 16 * b + i16;
+          if (i < d && j < d && i <= j) {
+            const float nv = S[i * d + j] + acc[a][b][v];
             S[i * d + j] = nv;
             if (i != j) S[j * d + i] = nv;
           }
         }
       }
   } else {
-    float* tile = part + ((int64_t(split) * upper_tiles(nt) + L) * kTile) * kTile;
+    // native accumulator order: one contiguous 256-byte store per (a, b, v)
+    float* dst = part + ((int64_t(split) * ntiles + upper_index(ti, tj, nt)) * 4 + wv) * kSubElems;
 #pragma unroll
-    for (int v = 0; v < 4; ++v)
+    for (int a = 0; a < 8; ++a)
 #pragma unroll
-      for (int f = 0; f < 8; ++f) {
-        const int a = 8 * (4 * g + v) + f;
-        f32x4 lo{acc[f][0][v], acc[f][1][v], acc[f][2][v], acc[f][3][v]};
-        f32x4 hi{acc[f][4][v], acc[f][5][v], acc[f][6][v], acc[f][7][v]};
-        *reinterpret_cast<f32x4*>(tile + a * kTile + 8 * fi) = lo;
-        *reinterpret_cast<f32x4*>(tile + a * kTile + 8 * fi + 4) = hi;
-      }
+      for (int b = 0; b < 8; ++b)
+#pragma unroll
+        for (int v = 0; v < 4; ++v)
+          dst[((a * 8 + b) * 4 + v) * 64 + lane] = acc[a][b][v];
   }
 }
 
-// Adds the split partials of every upper tile to S in split order (fp64
-// running sum) and mirrors the result into the lower triangle.
+// Adds the split partials of one 16 x 128 band (sub-tile wv, row block a) of
+// an upper super-tile to S in split order (fp64 running sum), then mirrors
+// the band into the lower triangle through LDS so both writes are row runs.
 __global__ __launch_bounds__(256) void hessian_reduce_kernel(
     const float* __restrict__ part, int64_t d, int nt, int nsplit,
     float* __restrict__ S) {
+  __shared__ float band[16][129];
   const int64_t L = blockIdx.x;
+  const int wv = blockIdx.y >> 3, a = blockIdx.y & 7;
   int ti, tj;
   tile_of(L, nt, ti, tj);
-  const int a = blockIdx.y * 2 + (threadIdx.x >> 7);
-  const int b = threadIdx.x & 127;
-  const int64_t i = int64_t(ti) * kTile + a, j = int64_t(tj) * kTile + b;
-  if (i >= d || j >= d || (ti == tj && a > b)) return;
+  const bool diag = ti == tj;
+  if (diag && wv == 2) return;
+  const int wa = wv >> 1, wb = wv & 1;
+  const int tid = threadIdx.x, v = tid >> 6, lane = tid & 63;
+  const int row = 4 * (lane >> 4) + v;
+  const int64_t i0 = int64_t(ti) * kSup + 128 * wa + 16 * a;
+  const int64_t j0 = int64_t(tj) * kSup + 128 * wb;
+  const int64_t i = i0 + row;
   const int64_t ntiles = upper_tiles(nt);
-  double sum = 0.0;
-  for (int s = 0; s < nsplit; ++s)
-    sum += part[((int64_t(s) * ntiles + L) * kTile + a) * kTile + b];
-  const float nv = static_cast<float>(static_cast<double>(S[i * d + j]) + sum);
-  S[i * d + j] = nv;
-  if (i != j) S[j * d + i] = nv;
+  const float* src = part + (L * 4 + wv) * kSubElems + a * 8 * 4 * 64 + v * 64 + lane;
+  const int64_t sstride = ntiles * 4 * kSubElems;
+  for (int b = 0; b < 8; ++b) {
+    const int col = 16 * b + (lane & 15);
+    const int64_t j = j0 + col;
+    double sum = 0.0;
+    for (int s = 0; s < nsplit; ++s) sum += src[s * sstride + b * 4 * 64];
+    float nv = 0.f;
+    if (i < d && j < d && (!diag || i <= j)) {
+      nv = static_cast<float>(static_cast<double>(S[i * d + j]) + sum);
+      S[i * d + j] = nv;
+    }
+    band[row][col] = nv;
+  }
+  __syncthreads();
+  const int r = tid & 15;
+#pragma unroll
+  for (int k = 0; k < 8; ++k) {
+    const int col = (tid >> 4) + 16 * k;
+    const int64_t ii = i0 + r, jj = j0 + col;
+    if (ii < d && jj < d && (!diag || ii < jj)) S[jj * d + ii] = band[r][col];
+  }
 }
 
 __device__ inline float to_f32(float x) { return x; }
@@ -330,27 +550,29 @@ struct SplitPlan {
   int64_t ks;
 };
 
-// Chooses the token split so the (tile x split) work items fill whole rounds
-// of one wave per SIMD, trading the tail-round loss against the partial-tile
-// traffic (written and read once, 64 KiB per tile and split).
+// Chooses the token split: (super-tile x split) work items run one workgroup
+// per CU, so the MFMA time is (rounds of kCUs items) x (steps per split); the
+// partial tiles cost a write and a read of 256 KiB per item.
 SplitPlan plan_splits(int64_t d, int64_t n_tok) {
-  const int64_t nt = (d + kTile - 1) / kTile;
+  const int64_t nt = (d + kSup - 1) / kSup;
   const int64_t ntiles = upper_tiles(nt);
-  const double mfma_s = 2.0 * double(n_tok) * double(d) * double(d) / 1.25e15;
-  const int max_split = static_cast<int>(std::max<int64_t>(1, (n_tok + 4095) / 4096));
-  SplitPlan best{1, n_tok};
+  const int64_t steps = (n_tok + kStep - 1) / kStep;
+  const double t_step = 1024.0 / 2.1e9;          // 64 MFMAs per SIMD per step
+  const double t_byte = 1.0 / 4.0e12;
+  SplitPlan best{1, steps * kStep};
   double best_t = 1e30;
-  for (int ns = 1; ns <= std::min(max_split, 64); ++ns) {
-    const int64_t ks = ((n_tok + ns - 1) / ns + kStep - 1) / kStep * kStep;
-    const int nsr = static_cast<int>((n_tok + ks - 1) / ks);
-    const int64_t items = ntiles * nsr;
-    const double rounds = double((items + kTargetWaves - 1) / kTargetWaves);
-    const double eff = double(items) / (rounds * kTargetWaves);
-    const double t = mfma_s / eff +
-                     (nsr > 1 ? 2.0 * nsr * ntiles * 65536.0 / 4.0e12 : 0.0);
+  const int64_t max_split = std::min<int64_t>(64, steps);
+  for (int64_t ns = 1; ns <= max_split; ++ns) {
+    // an even step count per split keeps every split but the last on the
+    // unmasked path
+    const int64_t per = ((steps + ns - 1) / ns + 1) & ~int64_t(1);
+    const int64_t nsr = (steps + per - 1) / per;
+    const int64_t rounds = (ntiles * nsr + kCUs - 1) / kCUs;
+    const double t = double(rounds) * double(per) * t_step +
+                     (nsr > 1 ? 2.0 * double(nsr * ntiles) * 4.0 * kSubElems * 4.0 * t_byte : 0.0);
     if (t < best_t * 0.999) {
       best_t = t;
-      best = SplitPlan{nsr, ks};
+      best = SplitPlan{static_cast<int>(nsr), per * kStep};
     }
   }
   return best;
@@ -362,16 +584,16 @@ size_t hessian_ws_bytes(int64_t d, int64_t n_tok) {
   if (d <= 0 || n_tok <= 0) return 0;
   const SplitPlan p = plan_splits(d, n_tok);
   if (p.nsplit <= 1) return 0;
-  const int64_t nt = (d + kTile - 1) / kTile;
-  return align_up(size_t(p.nsplit) * size_t(upper_tiles(nt)) * kTile * kTile * sizeof(float));
+  const int64_t nt = (d + kSup - 1) / kSup;
+  return align_up(size_t(p.nsplit) * size_t(upper_tiles(nt)) * 4 * kSubElems * sizeof(float));
 }
 
 namespace {
 bool mfma_path_ok(int64_t d, const void* X, gptq_dtype dt, int64_t ldx) {
-  // per-lane element offsets of a 32-token step are kept in 32 bits
+  // per-lane byte offsets of a 32-token step are kept in 32 bits
   return dt == GPTQ_BF16 && d % 8 == 0 && ldx % 8 == 0 &&
          reinterpret_cast<uintptr_t>(X) % 16 == 0 &&
-         int64_t(kStep) * ldx + d < (int64_t(1) << 32);
+         2 * (int64_t(kStep) * ldx + d) < (int64_t(1) << 32);
 }
 }  // namespace
 
@@ -391,15 +613,25 @@ gptq_status launch_hessian(float* S, int64_t d, const void* X, gptq_dtype dt,
     GPTQ_CHECK_LAUNCH();
     return GPTQ_OK;
   }
-  const int nt = static_cast<int>((d + kTile - 1) / kTile);
+  const int nt = static_cast<int>((d + kSup - 1) / kSup);
   const SplitPlan p = plan_splits(d, n_tok);
   const int64_t per_xcd = (upper_tiles(nt) + kXcd - 1) / kXcd;
-  hessian_bf16_kernel<<<dim3(static_cast<unsigned>(kXcd * per_xcd * p.nsplit)), 64, 0, st>>>(
+  const dim3 grid(static_cast<unsigned>(kXcd * per_xcd * p.nsplit));
+  hessian_bf16_kernel<true><<<grid, kThreads, 0, st>>>(
       static_cast<const uint16_t*>(X), ldx, n_tok, d, nt, p.ks, p.nsplit, S,
       static_cast<float*>(ws));
   GPTQ_CHECK_LAUNCH();
+  // masked items: panels crossing d, or a last split that is not a whole
+  // number of 32-token steps (every other split is, see plan_splits)
+  const int64_t last = n_tok - int64_t(p.nsplit - 1) * p.ks;
+  if (d % kSup != 0 || last % kStep != 0) {
+    hessian_bf16_kernel<false><<<grid, kThreads, 0, st>>>(
+        static_cast<const uint16_t*>(X), ldx, n_tok, d, nt, p.ks, p.nsplit, S,
+        static_cast<float*>(ws));
+    GPTQ_CHECK_LAUNCH();
+  }
   if (p.nsplit > 1) {
-    hessian_reduce_kernel<<<dim3(static_cast<unsigned>(upper_tiles(nt)), kTile / 2), 256, 0, st>>>(
+    hessian_reduce_kernel<<<dim3(static_cast<unsigned>(upper_tiles(nt)), 32), 256, 0, st>>>(
         static_cast<const float*>(ws), d, nt, p.nsplit, S);
     GPTQ_CHECK_LAUNCH();
   }
