@@ -88,17 +88,17 @@ gptq_status launch_init_work(const void* W, gptq_dtype dt, int64_t m,
                              int64_t d, int64_t ldw, const int32_t* perm,
                              const uint8_t* dead, float* WT, int32_t* pinv,
                              hipStream_t st);
-// RbT[blk] = transpose of R's diagonal block blk (blocks of bi columns).
-gptq_status launch_rbt(const float* R, int64_t d, int bi, float* RbT,
+// RL[blk] = R's diagonal block blk (blocks of bi <= 128 columns) in the chain
+// kernel's lane order, 128 x 128 floats per block.
+gptq_status launch_rbt(const float* R, int64_t d, int bi, float* RL,
                        hipStream_t st);
-// Block [i0, i0 + bw) of the column loop, in sub-blocks of sb <= 32 columns.
-// scalesP/zerosP are [n_g][m] (processing-group major); for group_size -1
-// row 0 holds the row grids.
-gptq_status launch_chain(float* WT, int64_t m, int64_t d, const float* RbT,
-                         int64_t i0, int bw, int sb, int bi,
-                         int bits, int64_t gsize, float* scalesP,
-                         uint8_t* zerosP, uint8_t* codesP, float* E,
-                         hipStream_t st);
+// Block [i0, i0 + bw) of the column loop (bw <= bi <= 128).  scalesP/zerosP
+// are [n_g][m] (processing-group major); for group_size -1 row 0 holds the
+// row grids.  Writes the block's codes and its residuals E [bw][m].
+gptq_status launch_chain(float* WT, int64_t m, int64_t d, const float* RL,
+                         int64_t i0, int bw, int bi, int bits, int64_t gsize,
+                         float* scalesP, uint8_t* zerosP, uint8_t* codesP,
+                         float* E, hipStream_t st);
 gptq_status launch_lazy_update(float* WT, int64_t m, int64_t d, const float* R,
                                int64_t i0, int bw, float* E,
                                hipStream_t st);

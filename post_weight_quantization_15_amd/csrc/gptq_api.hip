@@ -25,21 +25,6 @@ bool groups_fit_blocks(int64_t d, int64_t g, int64_t b) {
   return true;
 }
 
-// Same rule for the chain kernel's register sub-blocks of `sb` columns,
-// which restart at every block start.
-bool groups_fit_subblocks(int64_t d, int64_t g, int64_t bi, int64_t sb) {
-  if (g == -1) return true;
-  for (int64_t j = 0; j < d; j += g) {
-    const int64_t b0 = j / bi * bi;
-    const int64_t off = j - b0;
-    const int64_t s0 = off / sb * sb;
-    if (off == s0) continue;
-    const int64_t send = std::min(s0 + sb, std::min<int64_t>(bi, d - b0));
-    if (off + std::min<int64_t>(g, d - j) > send) return false;
-  }
-  return true;
-}
-
 bool valid_params(const gptq_params* p, int64_t d) {
   if (!p) return false;
   if (!(p->bits == 2 || p->bits == 3 || p->bits == 4 || p->bits == 8)) return false;
@@ -58,12 +43,6 @@ int internal_block(int64_t d, const gptq_params* p) {
   if (p->blocksize <= kChainMaxBlock) return p->blocksize;
   for (int bi = kChainMaxBlock; bi >= 1; --bi)
     if (p->blocksize % bi == 0 && groups_fit_blocks(d, p->group_size, bi)) return bi;
-  return 1;
-}
-
-int sub_block(int64_t d, const gptq_params* p, int bi) {
-  for (int sb = 32; sb > 1; sb /= 2)
-    if (sb <= bi && groups_fit_subblocks(d, p->group_size, bi, sb)) return sb;
   return 1;
 }
 
@@ -95,7 +74,7 @@ QuantWs carve_quant_ws(Carver& c, int64_t m, int64_t d, const gptq_params* p,
   q.scalesP = c.take<float>(size_t(ng) * size_t(m));
   q.zerosP = c.take<uint8_t>(size_t(ng) * size_t(m));
   q.pinv = c.take<int32_t>(size_t(d));
-  q.RbT = c.take<float>(size_t(nblk) * size_t(bi) * size_t(bi));
+  q.RbT = c.take<float>(size_t(nblk) * size_t(kChainMaxBlock) * size_t(kChainMaxBlock));
   if (factor_inside) {
     q.R = c.take<float>(size_t(d) * size_t(d));
     q.perm = c.take<int32_t>(size_t(d));
@@ -235,11 +214,10 @@ gptq_status gptq_quantize_layer(const void* W, gptq_dtype w_dtype, int64_t m,
   if ((s = launch_init_work(W, w_dtype, m, d, ldw, pu, du, q.WT, q.pinv, st)) != GPTQ_OK)
     return s;
   const int bi = internal_block(d, p);
-  const int sb = sub_block(d, p, bi);
   if ((s = launch_rbt(Ru, d, bi, q.RbT, st)) != GPTQ_OK) return s;
   for (int64_t i0 = 0; i0 < d; i0 += bi) {
     const int bw = static_cast<int>(std::min<int64_t>(bi, d - i0));
-    if ((s = launch_chain(q.WT, m, d, q.RbT, i0, bw, sb, bi, p->bits, gsize,
+    if ((s = launch_chain(q.WT, m, d, q.RbT, i0, bw, bi, p->bits, gsize,
                           q.scalesP, q.zerosP, q.codesP, q.E, st)) != GPTQ_OK)
       return s;
     if ((s = launch_lazy_update(q.WT, m, d, Ru, i0, bw, q.E, st)) != GPTQ_OK)

@@ -14,9 +14,11 @@
 // output rows), so reading a column, writing its codes and eta, and the
 // lazy update all stream contiguous memory.
 //
-// Chain kernel: one thread per output row (rows are independent given R and
-// their grids, [derivation] 2.3), the block's 128 columns in registers; the
-// R entries are wave-uniform loads.
+// Chain kernel: rows are independent given R and their grids ([derivation]
+// 2.3); each row is spread over the 16 lanes of one DPP row, lane q holding
+// the block columns q, q + 16, ..., q + 112 in registers.  Per column the
+// owning lane's residual is broadcast to the row with one DPP row_newbcast
+// and every lane updates its own later columns.
 // Lazy update: v_mfma_f32_16x16x4_f32 (exact fp32 products, fp32 sums).
 #include <algorithm>
 
@@ -25,10 +27,11 @@
 namespace gptq {
 namespace {
 
-constexpr int kB = 128;   // largest block handled by one chain launch
-constexpr int kSB = 32;   // sub-block held in registers
-constexpr int kCW = 4;    // waves per chain workgroup (64 rows each)
-constexpr int kRtPitch = kB + 4;   // LDS pitch of the R tile (16-byte rows)
+constexpr int kB = 128;        // largest block handled by one chain launch
+constexpr int kRowLanes = 16;  // lanes per output row (one DPP row)
+constexpr int kCols = kB / kRowLanes;   // block columns per lane
+constexpr int kChainRows = 16; // output rows per 256-thread workgroup
+constexpr int kTp = kChainRows + 1;     // LDS pitch of the row tiles
 
 __device__ inline float to_f32(float x) { return x; }
 __device__ inline float to_f32(uint16_t x) { return __uint_as_float(uint32_t(x) << 16); }
@@ -102,182 +105,199 @@ __global__ __launch_bounds__(256) void init_work_kernel(
   }
 }
 
-// Transposed diagonal blocks of R: RbT[blk][c][k] = R[i + k][i + c] for the
-// block starting at i = blk * bi (k <= c < bw), 0 elsewhere.  Column c of a
-// block's R is then contiguous for the batched in-block update below.
-__global__ __launch_bounds__(256) void rbt_kernel(const float* __restrict__ R,
-                                                  int64_t d, int bi,
-                                                  float* __restrict__ RbT) {
+// Diagonal blocks of R in the chain's lane order:
+// RL[blk][k][q][t] = R[i + k][i + q + 16 t] for the block starting at
+// i = blk * bi, k <= q + 16 t < bw (0 elsewhere, up to 128 x 128).  Row k
+// of a block is then one 32-byte run per lane q.
+__global__ __launch_bounds__(256) void rl_kernel(const float* __restrict__ R,
+                                                 int64_t d, int bi,
+                                                 float* __restrict__ RL) {
   const int64_t blk = blockIdx.y;
   const int64_t i = blk * bi;
   const int bw = static_cast<int>(min<int64_t>(bi, d - i));
-  for (int e = threadIdx.x + blockIdx.x * 256; e < bi * bi; e += 256 * gridDim.x) {
-    const int c = e / bi, k = e % bi;
-    RbT[blk * bi * bi + e] = (k <= c && c < bw) ? R[(i + k) * d + i + c] : 0.0f;
+  for (int e = threadIdx.x + blockIdx.x * 256; e < kB * kB; e += 256 * gridDim.x) {
+    const int k = e / kB, q = (e / kCols) % kRowLanes, t = e % kCols;
+    const int c = q + kRowLanes * t;
+    RL[blk * kB * kB + e] = (k <= c && c < bw) ? R[(i + k) * d + i + c] : 0.0f;
   }
 }
 
-// The column chain over one sub-block [s0, s0 + sw) held in registers.
-// FULL: sw == kSB, so no per-column guards are needed.
-template <int FS, bool FULL>
-__device__ __forceinline__ void chain_sub(
-    float (*rows)[64], float (*rt)[kRtPitch], const float* __restrict__ WT,
-    int64_t m, int64_t d, int64_t i0, int s0, int sw, int bw, float maxq,
-    int64_t gsize, int lane, int64_t rr, int64_t r, bool store, float& scale,
-    float& zero, float& inv_scale, float* __restrict__ scalesP,
-    uint8_t* __restrict__ zerosP, uint8_t* __restrict__ codesP,
-    float* __restrict__ E, float (&eta)[kSB]) {
-  float w[kSB], rinv[kSB];
-#pragma clang loop unroll(full)
-  for (int k = 0; k < kSB; ++k) {
-    const bool in = FULL || k < sw;
-    w[k] = in ? rows[s0 + k][lane] : 0.0f;
-    rinv[k] = in ? 1.0f / rt[s0 + k][s0 + k] : 0.0f;
-    eta[k] = 0.0f;
+__device__ inline float row_bcast(float x, int src) {
+  // DPP row_newbcast: lane src of every 16-lane row to the whole row
+  switch (src) {
+#define GPTQ_BC(L) case L: return __int_as_float(__builtin_amdgcn_update_dpp( \
+      0, __float_as_int(x), 0x150 + L, 0xF, 0xF, false));
+    GPTQ_BC(0) GPTQ_BC(1) GPTQ_BC(2) GPTQ_BC(3) GPTQ_BC(4) GPTQ_BC(5)
+    GPTQ_BC(6) GPTQ_BC(7) GPTQ_BC(8) GPTQ_BC(9) GPTQ_BC(10) GPTQ_BC(11)
+    GPTQ_BC(12) GPTQ_BC(13) GPTQ_BC(14) GPTQ_BC(15)
+#undef GPTQ_BC
   }
-#pragma clang loop unroll(full)
-  for (int k = 0; k < kSB; ++k) {
-    if (!FULL && k >= sw) break;
-    const int64_t col = i0 + s0 + k;
-    if (FS > 0 && (k % (FS > 0 ? FS : 1)) == 0 && (col % gsize) == 0) {
-      const int64_t gend = min(col + gsize, d);
-      float lo = 0.0f, hi = 0.0f;
-#pragma clang loop unroll(full)
-      for (int c = k; c < kSB; ++c)
-        if ((FULL || c < sw) && col - k + c < gend) {
-          lo = fminf(lo, w[c]);
-          hi = fmaxf(hi, w[c]);
-        }
-      for (int c = s0 + sw; c < bw && i0 + c < gend; ++c) {
-        const float x = rows[c][lane];
-        lo = fminf(lo, x);
-        hi = fmaxf(hi, x);
-      }
-      for (int64_t cc = i0 + bw; cc < gend; ++cc) {
-        const float x = WT[cc * m + rr];
-        lo = fminf(lo, x);
-        hi = fmaxf(hi, x);
-      }
-      fit_grid(lo, hi, maxq, scale, zero);
-      inv_scale = 1.0f / scale;
-      if (store) {
-        scalesP[(col / gsize) * m + r] = scale;
-        zerosP[(col / gsize) * m + r] = static_cast<uint8_t>(zero);
-      }
-    }
-    const float x = w[k];
-    const float c = fminf(fmaxf(rintf(x * inv_scale) + zero, 0.0f), maxq);
-    const float q = scale * (c - zero);
-    eta[k] = (x - q) * rinv[k];
-    if (store) {
-      codesP[col * m + r] = static_cast<uint8_t>(c);
-      E[(s0 + k) * m + r] = eta[k];
-    }
-    // columns past sw (ragged sub-block) are never read again
-#pragma clang loop unroll(full)
-    for (int k2 = k + 1; k2 < kSB; ++k2)
-      w[k2] = fmaf(-eta[k], rt[s0 + k2][s0 + k], w[k2]);
+  return x;
+}
+
+// min / max over the 16 lanes of a row
+__device__ inline void row_minmax(float& lo, float& hi) {
+#pragma unroll
+  for (int o = 1; o < kRowLanes; o <<= 1) {
+    lo = fminf(lo, __shfl_xor(lo, o));
+    hi = fmaxf(hi, __shfl_xor(hi, o));
   }
 }
 
-// One block [i0, i0 + bw) of the column loop.  A workgroup covers 64 output
-// rows with kCW waves.  The block is processed in sub-blocks of up to kSB
-// columns held in registers; every wave runs the same sub-block chain for
-// its 64 rows (identical inputs give identical results, so no cross-lane
-// exchange is needed) and the waves split the batched feedback of the
-// sub-block into the rest of the block, which lives in LDS.  This is the
-// in-block step of the column loop with lazy batching inside the block.
-// The block's R tile is staged transposed in LDS: rt[c][k] = R[i0+k][i0+c],
-// so every R read is a wave-uniform LDS broadcast.
-// FS: a dynamic group can only start at sub-block offsets that are
-// multiples of FS (0 = the whole-row grid, no refits).  Groups that start
-// inside a sub-block end inside it (checked on the host), so every fit sees
-// fully compensated columns.
-// Inside the chain the quotients w / Delta and rho / R_jj are products with
-// fp32 reciprocals; they differ from the IEEE quotients by at most an ulp,
-// which can only matter within 1e-6 of a rounding boundary.
-template <int FS>
-__global__ __launch_bounds__(64 * kCW) void chain_kernel(
-    float* __restrict__ WT, int64_t m, int64_t d, const float* __restrict__ RbT,
-    int64_t i0, int bw, int sb, int bi, float maxq, int64_t gsize,
+// One block [i0, i0 + bw) of the column loop for 16 output rows per
+// workgroup.  Thread (row rr = tid / 16, lane q = tid % 16) holds w[t] =
+// W_work[r0 + rr][i0 + q + 16 t].  For each column k (owner lane k % 16, slot
+// k / 16): every lane quantizes its slot-k/16 value, the owner's residual
+// eta = (w - q) / R_kk is broadcast over the row, and each lane applies
+// w[t] -= eta R[k][q + 16 t] for its later slots (R is upper triangular, so
+// slots at or before column k receive 0).  This is the in-block step of
+// the column loop ([derivation] eq. (42)); the block's R is read from LDS in
+// the RL lane order.
+// FS: a dynamic group can only start at block offsets that are multiples of
+// FS (0 = the whole-row grid, no refits).  A group that starts inside the
+// block ends inside it (checked on the host), so every fit sees fully
+// compensated columns; a group that starts at the block start and reaches
+// past it also reads its later columns from WT (compensated by every
+// earlier block).
+// The quotients w / Delta and rho / R_jj are products with fp32
+// reciprocals; they differ from the IEEE quotients by at most an ulp, which
+// can only matter within 1e-6 of a rounding boundary.
+template <int FS, bool VEC>
+__global__ __launch_bounds__(256) void chain_kernel(
+    const float* __restrict__ WT, int64_t m, int64_t d, const float* __restrict__ RL,
+    int64_t i0, int bw, int bi, float maxq, int64_t gsize,
     float* __restrict__ scalesP, uint8_t* __restrict__ zerosP,
     uint8_t* __restrict__ codesP, float* __restrict__ E) {
-  __shared__ float rows[kB][64];
-  __shared__ __attribute__((aligned(16))) float rt[kB][kRtPitch];
-  const int lane = threadIdx.x & 63;
-  const int wq = threadIdx.x >> 6;
-  const bool lead = wq == 0;
-  const int64_t r = int64_t(blockIdx.x) * 64 + lane;
+  __shared__ __attribute__((aligned(16))) float rl[kB * kB];
+  __shared__ float tile[kB][kTp];
+  __shared__ uint8_t ctile[kB][kChainRows];
+  const int tid = threadIdx.x;
+  const int rr = tid >> 4, q = tid & 15;
+  const int64_t r0 = int64_t(blockIdx.x) * kChainRows;
+  const int64_t r = r0 + rr;
   const bool act = r < m;
-  const int64_t rr = act ? r : 0;
-  // stage the transposed R tile and the block's columns of these rows
-  const float* rbt = RbT + (i0 / bi) * int64_t(bi) * bi;
+  const int64_t rs = act ? r : m - 1;
+  // stage RL of this block (contiguous 64 KiB) and the block's columns of the
+  // workgroup's rows (one 64-byte run per column)
   {
-    // all loads of this thread are issued before the first LDS store
-    float tb[2 * (kB / kCW)];
-#pragma clang loop unroll(full)
-    for (int u = 0; u < kB / kCW; ++u)
-#pragma clang loop unroll(full)
-      for (int h = 0; h < 2; ++h) {
-        const int c = wq + kCW * u, k = 64 * h + lane;
-        tb[2 * u + h] = (c < bw && k < bw) ? rbt[int64_t(c) * bi + k] : 0.0f;
-      }
-#pragma clang loop unroll(full)
-    for (int u = 0; u < kB / kCW; ++u)
-#pragma clang loop unroll(full)
-      for (int h = 0; h < 2; ++h) {
-        const int c = wq + kCW * u, k = 64 * h + lane;
-        if (c < bw && k < bw) rt[c][k] = tb[2 * u + h];
-      }
+    const f32x4* src = reinterpret_cast<const f32x4*>(RL + (i0 / bi) * int64_t(kB) * kB);
+    f32x4* dst = reinterpret_cast<f32x4*>(rl);
+    f32x4 buf[kB * kB / 4 / 256];
+#pragma unroll
+    for (int u = 0; u < kB * kB / 4 / 256; ++u) buf[u] = src[tid + 256 * u];
+#pragma unroll
+    for (int u = 0; u < kB * kB / 4 / 256; ++u) dst[tid + 256 * u] = buf[u];
   }
   {
-    float buf[kB / kCW];
-#pragma clang loop unroll(full)
-    for (int u = 0; u < kB / kCW; ++u) {
-      const int c = wq + kCW * u;
-      buf[u] = (c < bw) ? WT[(i0 + c) * m + rr] : 0.0f;
+    const int c = tid >> 1, h = tid & 1;
+    float v[8];
+    if (c < bw) {
+      const float* col = WT + (i0 + c) * m + r0 + 8 * h;
+      if (VEC && r0 + 8 * h + 8 <= m) {
+        const f32x4 a = *reinterpret_cast<const f32x4*>(col);
+        const f32x4 b = *reinterpret_cast<const f32x4*>(col + 4);
+        v[0] = a[0]; v[1] = a[1]; v[2] = a[2]; v[3] = a[3];
+        v[4] = b[0]; v[5] = b[1]; v[6] = b[2]; v[7] = b[3];
+      } else {
+#pragma unroll
+        for (int u = 0; u < 8; ++u) v[u] = (r0 + 8 * h + u < m) ? col[u] : 0.0f;
+      }
+    } else {
+#pragma unroll
+      for (int u = 0; u < 8; ++u) v[u] = 0.0f;
     }
-#pragma clang loop unroll(full)
-    for (int u = 0; u < kB / kCW; ++u) {
-      const int c = wq + kCW * u;
-      if (c < bw) rows[c][lane] = buf[u];
-    }
+#pragma unroll
+    for (int u = 0; u < 8; ++u) tile[c][8 * h + u] = v[u];
   }
   __syncthreads();
+  float w[kCols], rinv[kCols], eta[kCols], code[kCols];
+#pragma unroll
+  for (int t = 0; t < kCols; ++t) {
+    const int c = q + kRowLanes * t;
+    w[t] = tile[c][rr];
+    const float rjj = rl[(c * kRowLanes + q) * kCols + t];
+    rinv[t] = c < bw ? 1.0f / rjj : 0.0f;
+    eta[t] = 0.0f;
+    code[t] = 0.0f;
+  }
   // grid in force at the block start: the row grid, or the dynamic group
   // that contains column i0 (fitted by this launch if it starts here, by an
   // earlier launch otherwise)
   const int64_t g0 = (FS == 0) ? 0 : i0 / gsize;
-  float scale = scalesP[g0 * m + rr];
-  float zero = static_cast<float>(zerosP[g0 * m + rr]);
+  float scale = scalesP[g0 * m + rs];
+  float zero = static_cast<float>(zerosP[g0 * m + rs]);
   float inv_scale = 1.0f / scale;
-  for (int s0 = 0; s0 < bw; s0 += sb) {
-    const int sw = min(sb, bw - s0);
-    float eta[kSB];
-    if (sw == kSB)
-      chain_sub<FS, true>(rows, rt, WT, m, d, i0, s0, kSB, bw, maxq, gsize, lane,
-                          rr, r, lead && act, scale, zero, inv_scale, scalesP,
-                          zerosP, codesP, E, eta);
-    else
-      chain_sub<FS, false>(rows, rt, WT, m, d, i0, s0, sw, bw, maxq, gsize, lane,
-                           rr, r, lead && act, scale, zero, inv_scale, scalesP,
-                           zerosP, codesP, E, eta);
-    // feedback of this sub-block into the rest of the block, split by wave
-    if (sw == kSB) {
-      for (int c = s0 + sw + wq; c < bw; c += kCW) {
-        float x = rows[c][lane];
 #pragma clang loop unroll(full)
-        for (int k = 0; k < kSB; ++k) x = fmaf(-eta[k], rt[c][s0 + k], x);
-        rows[c][lane] = x;
+  for (int tk = 0; tk < kCols; ++tk) {
+#pragma clang loop unroll(full)
+  for (int qk = 0; qk < kRowLanes; ++qk) {
+    const int k = kRowLanes * tk + qk;
+    if (k >= bw) continue;      // uniform: columns past a partial block
+    if (FS > 0 && k % (FS > 0 ? FS : 1) == 0 && (i0 + k) % gsize == 0) {
+      const int64_t col = i0 + k;
+      const int64_t gend = min(col + gsize, d);
+      float lo = 0.0f, hi = 0.0f;
+#pragma unroll
+      for (int t = tk; t < kCols; ++t) {
+        const int64_t c = i0 + q + kRowLanes * t;
+        if (c >= col && c < gend && c < i0 + bw) {
+          lo = fminf(lo, w[t]);
+          hi = fmaxf(hi, w[t]);
+        }
       }
-    } else {
-      for (int c = s0 + sw + wq; c < bw; c += kCW) {
-        float x = rows[c][lane];
-        for (int k = 0; k < sw; ++k) x = fmaf(-eta[k], rt[c][s0 + k], x);
-        rows[c][lane] = x;
+      for (int64_t cc = i0 + bw + q; cc < gend; cc += kRowLanes) {
+        const float x = WT[cc * m + rs];
+        lo = fminf(lo, x);
+        hi = fmaxf(hi, x);
+      }
+      row_minmax(lo, hi);
+      fit_grid(lo, hi, maxq, scale, zero);
+      inv_scale = 1.0f / scale;
+      if (q == 0 && act) {
+        scalesP[(col / gsize) * m + r] = scale;
+        zerosP[(col / gsize) * m + r] = static_cast<uint8_t>(zero);
       }
     }
-    __syncthreads();
+    const float x = w[tk];
+    const float c = fminf(fmaxf(rintf(x * inv_scale) + zero, 0.0f), maxq);
+    const float e = (x - scale * (c - zero)) * rinv[tk];
+    if (q == qk) {
+      code[tk] = c;
+      eta[tk] = e;
+    }
+    const float eb = row_bcast(e, qk);
+    const float* rk = rl + (k * kRowLanes + q) * kCols;
+    if (tk < 4) {
+      const f32x4 ra = *reinterpret_cast<const f32x4*>(rk);
+#pragma unroll
+      for (int t = tk; t < 4; ++t) w[t] = fmaf(-eb, ra[t], w[t]);
+    }
+    const f32x4 rb = *reinterpret_cast<const f32x4*>(rk + 4);
+#pragma unroll
+    for (int t = (tk > 4 ? tk : 4); t < kCols; ++t) w[t] = fmaf(-eb, rb[t - 4], w[t]);
+  }
+  }
+  // codes and residuals out through LDS, one coalesced run per column
+  __syncthreads();
+#pragma unroll
+  for (int t = 0; t < kCols; ++t) {
+    const int cidx = q + kRowLanes * t;
+    tile[cidx][rr] = eta[t];
+    ctile[cidx][rr] = static_cast<uint8_t>(code[t]);
+  }
+  __syncthreads();
+  {
+    const int c = tid >> 1, h = tid & 1;
+    if (c < bw) {
+      float* erow = E + int64_t(c) * m + r0 + 8 * h;
+      uint8_t* crow = codesP + (i0 + c) * m + r0 + 8 * h;
+#pragma unroll
+      for (int u = 0; u < 8; ++u)
+        if (r0 + 8 * h + u < m) {
+          erow[u] = tile[c][8 * h + u];
+          crow[u] = ctile[c][8 * h + u];
+        }
+    }
   }
 }
 
@@ -426,39 +446,47 @@ gptq_status launch_init_work(const void* W, gptq_dtype dt, int64_t m,
   return GPTQ_OK;
 }
 
-gptq_status launch_rbt(const float* R, int64_t d, int bi, float* RbT,
+gptq_status launch_rbt(const float* R, int64_t d, int bi, float* RL,
                        hipStream_t st) {
   const int64_t nblk = (d + bi - 1) / bi;
-  rbt_kernel<<<dim3(cdiv(int64_t(bi) * bi, 256 * 8), static_cast<unsigned>(nblk)), 256, 0, st>>>(R, d, bi, RbT);
+  rl_kernel<<<dim3(8, static_cast<unsigned>(nblk)), 256, 0, st>>>(R, d, bi, RL);
   GPTQ_CHECK_LAUNCH();
   return GPTQ_OK;
 }
 
-gptq_status launch_chain(float* WT, int64_t m, int64_t d, const float* RbT,
-                         int64_t i0, int bw, int sb, int bi,
-                         int bits, int64_t gsize, float* scalesP,
-                         uint8_t* zerosP, uint8_t* codesP, float* E,
-                         hipStream_t st) {
+gptq_status launch_chain(float* WT, int64_t m, int64_t d, const float* RL,
+                         int64_t i0, int bw, int bi, int bits, int64_t gsize,
+                         float* scalesP, uint8_t* zerosP, uint8_t* codesP,
+                         float* E, hipStream_t st) {
   const float maxq = static_cast<float>((1 << bits) - 1);
   int fs = 0;
   if (gsize > 0) {
     fs = 1;
-    while (fs < kSB && gsize % (2 * fs) == 0) fs *= 2;
+    while (fs < kB && gsize % (2 * fs) == 0) fs *= 2;
   }
-  const dim3 grid(cdiv(m, 64));
-#define GPTQ_CHAIN(FSV)                                                        \
-  chain_kernel<FSV><<<grid, 64 * kCW, 0, st>>>(WT, m, d, RbT, i0, bw, sb, bi, \
-                                                maxq, gsize, scalesP, zerosP,  \
-                                                codesP, E)
-  switch (fs) {
-    case 0: GPTQ_CHAIN(0); break;
-    case 1: GPTQ_CHAIN(1); break;
-    case 2: GPTQ_CHAIN(2); break;
-    case 4: GPTQ_CHAIN(4); break;
-    case 8: GPTQ_CHAIN(8); break;
-    case 16: GPTQ_CHAIN(16); break;
-    default: GPTQ_CHAIN(32); break;
+  const bool vec = m % 4 == 0 && reinterpret_cast<uintptr_t>(WT) % 16 == 0;
+  const dim3 grid(cdiv(m, kChainRows));
+#define GPTQ_CHAIN(FSV, V)                                                     \
+  chain_kernel<FSV, V><<<grid, 256, 0, st>>>(WT, m, d, RL, i0, bw, bi, maxq,  \
+                                             gsize, scalesP, zerosP, codesP, E)
+#define GPTQ_CHAIN_FS(V)                     \
+  switch (fs) {                              \
+    case 0: GPTQ_CHAIN(0, V); break;         \
+    case 1: GPTQ_CHAIN(1, V); break;         \
+    case 2: GPTQ_CHAIN(2, V); break;         \
+    case 4: GPTQ_CHAIN(4, V); break;         \
+    case 8: GPTQ_CHAIN(8, V); break;         \
+    case 16: GPTQ_CHAIN(16, V); break;       \
+    case 32: GPTQ_CHAIN(32, V); break;       \
+    case 64: GPTQ_CHAIN(64, V); break;       \
+    default: GPTQ_CHAIN(128, V); break;      \
   }
+  if (vec) {
+    GPTQ_CHAIN_FS(true)
+  } else {
+    GPTQ_CHAIN_FS(false)
+  }
+#undef GPTQ_CHAIN_FS
 #undef GPTQ_CHAIN
   GPTQ_CHECK_LAUNCH();
   return GPTQ_OK;
