@@ -27,6 +27,10 @@ HIPCC_FLAGS = [
 ]
 
 
+# Per-file additions (none at present).
+FILE_FLAGS: dict = {}
+
+
 def hipcc() -> str:
     path = shutil.which("hipcc") or "/opt/rocm/bin/hipcc"
     if not os.path.exists(path):
@@ -44,7 +48,7 @@ def build(verbose: bool = False) -> str:
     for src in srcs:
         obj = os.path.join(BUILD, os.path.basename(src)[:-4] + ".o")
         objs.append(obj)
-        cmd = [cc, *HIPCC_FLAGS, "-c", src, "-o", obj]
+        cmd = [cc, *HIPCC_FLAGS, *FILE_FLAGS.get(os.path.basename(src), []), "-c", src, "-o", obj]
         if verbose:
             print(" ".join(cmd), flush=True)
         procs.append((src, subprocess.Popen(cmd, stdout=subprocess.PIPE,

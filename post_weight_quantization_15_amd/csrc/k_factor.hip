@@ -16,7 +16,9 @@
 //   1. factor the diagonal block A_KK = U_KK U_KK^T and invert it,
 //      W_KK = U_KK^-1 (= R's diagonal block), in one workgroup;
 //   2. panel: U_iK = A_iK W_KK^T for every row i above the block (GEMM);
-//   3. trailing update A_ij -= U_iK U_jK^T (upper tiles only).
+//   3. trailing update A_ij -= U_iK U_jK^T (upper tiles only), applied to
+//      the next blocks' own columns at once and to the rest of the matrix
+//      once per group of four blocks (k = 256).
 // The off-diagonal blocks of R then come from R_12 = -R_11 U_12 R_22
 // applied level by level (block size 64, 128, 256, ...).
 #include <algorithm>
@@ -28,6 +30,7 @@ namespace gptq {
 namespace {
 
 constexpr int kNb = 64;          // diagonal block / panel width
+constexpr int kGroup = 4;        // blocks per trailing update (k = 256)
 constexpr double kEpsFloor = 1.1920928955078125e-07;   // 2^-23
 
 // ---------------------------------------------------------------------------
@@ -370,10 +373,10 @@ __device__ inline void zero_acc(f64x4 acc[2][2]) {
 }
 
 // Step 3: A[i][j] -= sum_c P[i][c] P[j][c] over the upper 64x64 tiles of
-// [0, k0)^2, P = H[:, k0:k0+nbk].
+// [0, k0)^2 whose tile column is tj0 + blockIdx.x, P = H[:, k0:k0+nbk].
 __global__ __launch_bounds__(256) void syrk_update_kernel(
-    double* __restrict__ H, int64_t d, int64_t k0, int nbk) {
-  const int64_t ti = blockIdx.y, tj = blockIdx.x;
+    double* __restrict__ H, int64_t d, int64_t k0, int nbk, int64_t tj0) {
+  const int64_t ti = blockIdx.y, tj = tj0 + blockIdx.x;
   if (ti > tj) return;
   const int64_t I0 = ti * 64, J0 = tj * 64;
   const double* P = H + k0;
@@ -546,21 +549,37 @@ gptq_status launch_cholesky_upper(int64_t d, const FactorWs& f,
                                   hipStream_t st) {
   zero_flag_kernel<<<1, 1, 0, st>>>(f.flag);
   GPTQ_CHECK_LAUNCH();
-  // blocks from the bottom-right corner; the first one absorbs d % 64
+  // 64-column blocks, 64-aligned from the top (the bottom one absorbs
+  // d % 64), taken from the bottom in groups of kGroup.  Inside a group each
+  // block gets the contributions of the group's blocks below it only on its
+  // own column tile; the rest of the trailing matrix receives the whole
+  // group at once, one update with k = up to 64 kGroup.
   int64_t k1 = d;
   while (k1 > 0) {
-    const int nbk = static_cast<int>((k1 % kNb) ? (k1 % kNb) : kNb);
-    const int64_t k0 = k1 - nbk;
-    chol_diag_kernel<<<1, 256, 0, st>>>(f.H, f.R, d, k0, nbk, f.flag);
-    GPTQ_CHECK_LAUNCH();
-    if (k0 > 0) {
-      chol_panel_kernel<<<cdiv(k0, 64), 256, 0, st>>>(f.H, f.R, d, k0, nbk);
+    const int64_t kend = k1;
+    for (int x = 0; x < kGroup && k1 > 0; ++x) {
+      const int nbk = static_cast<int>((k1 % kNb) ? (k1 % kNb) : kNb);
+      const int64_t k0 = k1 - nbk;
+      if (x > 0) {
+        // A[i][j] -= U[i][k1:kend] U[j][k1:kend]^T for j in this block, i <= j
+        syrk_update_kernel<<<dim3(1, cdiv(k1, 64)), 256, 0, st>>>(
+            f.H, d, k1, static_cast<int>(kend - k1), k0 / 64);
+        GPTQ_CHECK_LAUNCH();
+      }
+      chol_diag_kernel<<<1, 256, 0, st>>>(f.H, f.R, d, k0, nbk, f.flag);
       GPTQ_CHECK_LAUNCH();
-      const unsigned nt = cdiv(k0, 64);
-      syrk_update_kernel<<<dim3(nt, nt), 256, 0, st>>>(f.H, d, k0, nbk);
+      if (k0 > 0) {
+        chol_panel_kernel<<<cdiv(k0, 64), 256, 0, st>>>(f.H, f.R, d, k0, nbk);
+        GPTQ_CHECK_LAUNCH();
+      }
+      k1 = k0;
+    }
+    if (k1 > 0) {
+      const unsigned nt = cdiv(k1, 64);
+      syrk_update_kernel<<<dim3(nt, nt), 256, 0, st>>>(
+          f.H, d, k1, static_cast<int>(kend - k1), 0);
       GPTQ_CHECK_LAUNCH();
     }
-    k1 = k0;
   }
   return GPTQ_OK;
 }
