@@ -41,6 +41,8 @@ constexpr int kSubElems = 128 * 128;           // one wave's partial tile
 constexpr int kCUs = 256;                      // MI355X compute units
 constexpr int kXcd = 8;                        // accelerator dies, own L2 each
 constexpr int kRegB = 4;                       // XCD regions: blocks of 4x4 super-tiles
+constexpr int64_t kMaxChain = 2048;            // steps per fp32 running sum (see plan_splits)
+constexpr double kMaxPartBytes = 16.0 * (1 << 30);
 
 __host__ __device__ inline int64_t upper_tiles(int64_t nt) { return nt * (nt + 1) / 2; }
 
@@ -552,7 +554,10 @@ struct SplitPlan {
 
 // Chooses the token split: (super-tile x split) work items run one workgroup
 // per CU, so the MFMA time is (rounds of kCUs items) x (steps per split); the
-// partial tiles cost a write and a read of 256 KiB per item.
+// partial tiles cost a write and a read of 256 KiB per item.  Each split is
+// one fp32 running sum per entry; splits of at most kMaxChain steps bound its
+// rounding error (~steps * 2^-24 relative), as long as the partial tiles fit
+// in kMaxPartBytes.
 SplitPlan plan_splits(int64_t d, int64_t n_tok) {
   const int64_t nt = (d + kSup - 1) / kSup;
   const int64_t ntiles = upper_tiles(nt);
@@ -562,7 +567,12 @@ SplitPlan plan_splits(int64_t d, int64_t n_tok) {
   SplitPlan best{1, steps * kStep};
   double best_t = 1e30;
   const int64_t max_split = std::min<int64_t>(64, steps);
-  for (int64_t ns = 1; ns <= max_split; ++ns) {
+  const double part_item = 4.0 * kSubElems * 4.0;
+  int64_t min_split = 1;
+  while (min_split < max_split && (steps + min_split - 1) / min_split > kMaxChain &&
+         double(min_split + 1) * double(ntiles) * part_item <= kMaxPartBytes)
+    ++min_split;
+  for (int64_t ns = min_split; ns <= max_split; ++ns) {
     // an even step count per split keeps every split but the last on the
     // unmasked path
     const int64_t per = ((steps + ns - 1) / ns + 1) & ~int64_t(1);

@@ -93,13 +93,19 @@ def unpack_gpu(qweight, d, bits):
     return orc.unpack_codes(np.asarray(qweight).view(np.uint32), d, bits)
 
 
-def compare_layer(res, W, S, n, gpu, params, check_w_hat=True):
+def compare_layer(res, W, S, n, gpu, params, check_w_hat=True, sampled_rows=False):
     """Full comparison of one quantized layer.
 
     res: oracle GPTQResult from the same inputs; W: original weights (f64
     numpy); S: oracle statistics; gpu: dict of numpy arrays from the HIP path
     (qweight, scales, zeros, g_idx, optionally w_hat).  Returns a report and
     raises AssertionError on any failure.
+
+    sampled_rows: W and gpu hold a sample of a layer's rows.  A row whose
+    trajectory left the oracle's at an excused near-tie is another valid
+    GPTQ result with its own error, which a handful of rows cannot average
+    out; the layer-error bound then covers the rows that did not diverge
+    (the same trajectory), and the diverged rows are bounded in number.
     """
     bits, g, b = params["bits"], params["group_size"], params["blocksize"]
     m, d = W.shape
@@ -181,8 +187,14 @@ def compare_layer(res, W, S, n, gpu, params, check_w_hat=True):
     report["unique_frac"] = float(pref.mean())
     report["w_hat_rel_all"] = float(np.linalg.norm(w_hat_codes - res.w_hat) /
                                     max(np.linalg.norm(res.w_hat), 1e-30))
-    L_orc = orc.layer_error(W, res.w_hat, S, n)
-    L_gpu = orc.layer_error(W, w_hat_codes, S, n)
+    keep = np.ones(m, dtype=bool)
+    if sampled_rows:
+        keep = first >= d
+        report["rows_compared_for_layer_error"] = int(keep.sum())
+        if keep.sum() < max(1, (3 * m) // 4):
+            problems.append(f"{m - int(keep.sum())} of {m} sampled rows diverged")
+    L_orc = orc.layer_error(W[keep], res.w_hat[keep], S, n) if keep.any() else 0.0
+    L_gpu = orc.layer_error(W[keep], w_hat_codes[keep], S, n) if keep.any() else 0.0
     rel_L = abs(L_gpu - L_orc) / max(L_orc, 1e-300)
     report.update(w_hat_rel=float(rel_w), layer_err_rel=float(rel_L),
                   layer_err=float(L_orc))
