@@ -152,15 +152,24 @@ constexpr int kWp = kNb + 2;     // LDS pitch of the U / W arrays (16-B rows)
 // W_KK = U_KK^-1 (R's diagonal block, R = U^-1): the four 16 x 16 diagonal
 // blocks by back substitution, then W_12 = -W_11 U_12 W_22 at sizes 16 and
 // 32 on the matrix cores.
-__global__ __launch_bounds__(256) void chol_diag_kernel(
-    double* __restrict__ H, double* __restrict__ R, int64_t d, int64_t k0,
-    int nbk, int* __restrict__ flag) {
+struct DiagLds {
+  double Us[kNb][kWp];   // block staging, then U
+  double Wl[kNb][kWp];   // W = U^-1
+  double pan[2][4][kNb];
+  double rsl[kNb];       // 1 / U_cc
+  double Tl[32][34];
+};
+
+// Factor and invert the diagonal block into L.Us (U, upper, identity-padded)
+// and L.Wl (W = U^-1); returns true when a pivot was not positive.
+__device__ inline bool diag_factor(const double* __restrict__ H, int64_t d,
+                                   int64_t k0, int nbk, DiagLds& L) {
   static_assert(kNb == 64, "thread/element split assumes 64 columns");
-  __shared__ __align__(16) double Us[kNb][kWp];   // block staging, then U
-  __shared__ __align__(16) double Wl[kNb][kWp];   // W = U^-1
-  __shared__ double pan[2][4][kNb];
-  __shared__ double rsl[kNb];                     // 1 / U_cc
-  __shared__ __align__(16) double Tl[32][34];
+  auto& Us = L.Us;
+  auto& Wl = L.Wl;
+  auto& pan = L.pan;
+  auto& rsl = L.rsl;
+  auto& Tl = L.Tl;
   const int t = threadIdx.x;
   const int w = t >> 6, i = t & 63;
   for (int e = t; e < kNb * kNb; e += 256) {
@@ -217,7 +226,6 @@ __global__ __launch_bounds__(256) void chol_diag_kernel(
       a[u] = v;
     }
   }
-  if (bad && t == 0) atomicOr(flag, 1);
   __syncthreads();
   const int lane = i, lr = lane & 15, lk = lane >> 4;
   // 16 x 16 diagonal blocks of W: wave w, lanes 0..15 solve one column each
@@ -274,10 +282,28 @@ __global__ __launch_bounds__(256) void chol_diag_kernel(
     for (int v = 0; v < 4; ++v) Wl[r0 + lk + 4 * v][32 + c0 + lr] = -Y[v];
   }
   __syncthreads();
+  return bad;
+}
+
+// Writes W_KK (R's diagonal block; U_KK itself is not needed later) and
+// raises the flag on a non-positive pivot.
+__device__ inline void diag_store(double* __restrict__ R, int64_t d, int64_t k0,
+                                  int nbk, bool bad, const DiagLds& L,
+                                  int* __restrict__ flag) {
+  const int t = threadIdx.x;
+  if (bad && t == 0) atomicOr(flag, 1);
   for (int e = t; e < kNb * kNb; e += 256) {
     const int r = e >> 6, c = e & 63;
-    if (r < nbk && c < nbk) R[(k0 + r) * d + k0 + c] = (r <= c) ? Wl[r][c] : 0.0;
+    if (r < nbk && c < nbk) R[(k0 + r) * d + k0 + c] = (r <= c) ? L.Wl[r][c] : 0.0;
   }
+}
+
+__global__ __launch_bounds__(256) void chol_diag_kernel(
+    double* __restrict__ H, double* __restrict__ R, int64_t d, int64_t k0,
+    int nbk, int* __restrict__ flag) {
+  __shared__ __align__(16) DiagLds L;
+  const bool bad = diag_factor(H, d, k0, nbk, L);
+  diag_store(R, d, k0, nbk, bad, L, flag);
 }
 
 // ---------------------------------------------------------------------------
