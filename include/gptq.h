@@ -19,11 +19,13 @@
  *     between calls.  Calls that share a workspace must not overlap.
  *   - `stream` is a hipStream_t passed as void* (NULL = the default stream).
  *     Work is enqueued on it in order.  gptq_cholesky_inverse and
- *     gptq_quantize_layer (when it factors) synchronise `stream` once to read
- *     the positive-definiteness flag.
+ *     gptq_quantize_layer (when it factors) enqueue all of a damping
+ *     attempt's work, then synchronise `stream` once to read the
+ *     positive-definiteness flag; a failed attempt is redone whole.
  *   - Matrices are row-major with an explicit leading dimension.
- *   - Every argument is validated before anything is enqueued; a failing call
- *     returns a status and leaves outputs untouched.  Nothing is thrown
+ *   - Every argument is validated before anything is enqueued; a call that
+ *     fails validation returns a status and leaves outputs untouched (NOT_SPD
+ *     is reported after the work ran; see the factor).  Nothing is thrown
  *     across the ABI.
  */
 #ifndef GPTQ_MI355_H
@@ -101,7 +103,8 @@ gptq_status gptq_hessian_accumulate(float* S, int64_t d, const void* X,
  *          dead uint8 [d] (original order); *damp_used [host] (may be NULL).
  * ws: at least gptq_factor_workspace_bytes(d).
  * Errors: INVALID_ARG (d <= 0, n <= 0, percdamp < 0 or NaN, NULL outputs);
- *         WORKSPACE; NOT_SPD (*damp_used = last damping tried); HIP.
+ *         WORKSPACE; NOT_SPD (*damp_used = last damping tried; R, perm and
+ *         dead then hold the last attempt's values, R meaningless); HIP.
  * ------------------------------------------------------------------------- */
 size_t gptq_factor_workspace_bytes(int64_t d);
 gptq_status gptq_cholesky_inverse(const float* S, int64_t n, int64_t d,
@@ -135,7 +138,7 @@ gptq_status gptq_cholesky_inverse(const float* S, int64_t n, int64_t d,
  *     only when the factor is computed internally: pass factor_inside = 1).
  * Errors: INVALID_ARG (m, d <= 0, ldw < d, bad params, mixed NULL-ness of
  *         R/perm/dead, NULL S when factoring, NULL outputs); WORKSPACE;
- *         NOT_SPD; HIP.
+ *         NOT_SPD (the outputs then hold meaningless values); HIP.
  * ------------------------------------------------------------------------- */
 size_t gptq_workspace_bytes(int64_t m, int64_t d, const gptq_params* p,
                             int32_t factor_inside);

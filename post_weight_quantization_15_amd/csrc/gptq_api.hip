@@ -84,29 +84,81 @@ QuantWs carve_quant_ws(Carver& c, int64_t m, int64_t d, const gptq_params* p,
   return q;
 }
 
+// One damping attempt of the factor: enqueues everything up to R (fp32).
+// The Cholesky raises f.flag on a non-positive pivot; the kernels after it
+// do plain arithmetic (no value-dependent addressing), so they may run on a
+// failed factor and the caller reads the flag once, after the whole
+// attempt's work -- the factor and whatever consumes R -- is enqueued.
+gptq_status enqueue_factor(const float* S, int64_t n, int64_t d, float percdamp,
+                           int act_order, int attempt, float* R, int32_t* perm,
+                           uint8_t* dead, const FactorWs& f, hipStream_t st) {
+  gptq_status s;
+  if ((s = launch_prep_stats(S, d, n, percdamp, attempt, f, dead, st)) != GPTQ_OK) return s;
+  if (attempt == 0 && (s = launch_perm(d, act_order, f, perm, st)) != GPTQ_OK) return s;
+  if ((s = launch_build_h(S, d, n, perm, dead, f, st)) != GPTQ_OK) return s;
+  if ((s = launch_cholesky_upper(d, f, st)) != GPTQ_OK) return s;
+  if ((s = launch_triangular_inverse(d, f, st)) != GPTQ_OK) return s;
+  return launch_r_to_f32(d, f, R, st);
+}
+
+// Waits for the stream and reads the attempt's outcome.
+gptq_status read_factor_outcome(const FactorWs& f, hipStream_t st, bool* ok,
+                                double* damp) {
+  int flag = 0;
+  GPTQ_CHECK_HIP(hipMemcpyAsync(&flag, f.flag, sizeof(int), hipMemcpyDeviceToHost, st));
+  GPTQ_CHECK_HIP(hipMemcpyAsync(damp, f.damp, sizeof(double), hipMemcpyDeviceToHost, st));
+  GPTQ_CHECK_HIP(hipStreamSynchronize(st));
+  *ok = flag == 0;
+  return GPTQ_OK;
+}
+
 gptq_status run_factor(const float* S, int64_t n, int64_t d, float percdamp,
                        int act_order, float* R, int32_t* perm, uint8_t* dead,
                        float* damp_used, const FactorWs& f, hipStream_t st) {
   double damp = 0.0;
   for (int attempt = 0; attempt <= kMaxRetries; ++attempt) {
     gptq_status s;
-    if ((s = launch_prep_stats(S, d, n, percdamp, attempt, f, dead, st)) != GPTQ_OK) return s;
-    if (attempt == 0 && (s = launch_perm(d, act_order, f, perm, st)) != GPTQ_OK) return s;
-    if ((s = launch_build_h(S, d, n, perm, dead, f, st)) != GPTQ_OK) return s;
-    if ((s = launch_cholesky_upper(d, f, st)) != GPTQ_OK) return s;
-    int flag = 0;
-    GPTQ_CHECK_HIP(hipMemcpyAsync(&flag, f.flag, sizeof(int), hipMemcpyDeviceToHost, st));
-    GPTQ_CHECK_HIP(hipMemcpyAsync(&damp, f.damp, sizeof(double), hipMemcpyDeviceToHost, st));
-    GPTQ_CHECK_HIP(hipStreamSynchronize(st));
-    if (flag == 0) {
-      if ((s = launch_triangular_inverse(d, f, st)) != GPTQ_OK) return s;
-      if ((s = launch_r_to_f32(d, f, R, st)) != GPTQ_OK) return s;
+    if ((s = enqueue_factor(S, n, d, percdamp, act_order, attempt, R, perm, dead, f, st)) != GPTQ_OK)
+      return s;
+    bool ok = false;
+    if ((s = read_factor_outcome(f, st, &ok, &damp)) != GPTQ_OK) return s;
+    if (ok) {
       if (damp_used) *damp_used = static_cast<float>(damp);
       return GPTQ_OK;
     }
   }
   if (damp_used) *damp_used = static_cast<float>(damp);
   return GPTQ_ERR_NOT_SPD;
+}
+
+// The column loop and the outputs for one layer, given the factor.
+gptq_status enqueue_columns(const void* W, gptq_dtype w_dtype, int64_t m,
+                            int64_t d, int64_t ldw, const gptq_params* p,
+                            const float* Ru, const int32_t* pu,
+                            const uint8_t* du, const QuantWs& q,
+                            uint32_t* qweight, float* scales, uint8_t* zeros,
+                            int32_t* g_idx, float* w_hat, hipStream_t st) {
+  gptq_status s;
+  const int64_t gsize = p->group_size;
+  // whole-row grid on the original row, before dead columns are zeroed
+  if (gsize == -1 &&
+      (s = launch_fit_rows(W, w_dtype, m, d, ldw, p->bits, q.scalesP, q.zerosP, st)) != GPTQ_OK)
+    return s;
+  if ((s = launch_init_work(W, w_dtype, m, d, ldw, pu, du, q.WT, q.pinv, st)) != GPTQ_OK)
+    return s;
+  const int bi = internal_block(d, p);
+  if ((s = launch_rbt(Ru, d, bi, q.RbT, st)) != GPTQ_OK) return s;
+  for (int64_t i0 = 0; i0 < d; i0 += bi) {
+    const int bw = static_cast<int>(std::min<int64_t>(bi, d - i0));
+    if ((s = launch_chain(q.WT, m, d, q.RbT, i0, bw, bi, p->bits, gsize,
+                          q.scalesP, q.zerosP, q.codesP, q.E, st)) != GPTQ_OK)
+      return s;
+    if ((s = launch_lazy_update(q.WT, m, d, Ru, i0, bw, q.E, st)) != GPTQ_OK)
+      return s;
+  }
+  return launch_outputs(m, d, p->bits, static_cast<int>(gsize), q.codesP,
+                        q.scalesP, q.zerosP, q.pinv, q.codesO, qweight, scales,
+                        zeros, g_idx, w_hat, st);
 }
 
 }  // namespace
@@ -194,38 +246,25 @@ gptq_status gptq_quantize_layer(const void* W, gptq_dtype w_dtype, int64_t m,
   QuantWs q = carve_quant_ws(c, m, d, p, factor_inside);
   if (!ws || ws_bytes < c.bytes()) return GPTQ_ERR_WORKSPACE;
   hipStream_t st = static_cast<hipStream_t>(stream);
-  gptq_status s;
-  const float* Ru = R;
-  const int32_t* pu = perm;
-  const uint8_t* du = dead;
-  if (factor_inside) {
-    if ((s = run_factor(S, n, d, p->percdamp, p->act_order, q.R, q.perm, q.dead,
-                        nullptr, q.f, st)) != GPTQ_OK)
+  if (!factor_inside)
+    return enqueue_columns(W, w_dtype, m, d, ldw, p, R, perm, dead, q, qweight,
+                           scales, zeros, g_idx, w_hat, st);
+  // The whole layer is enqueued behind each damping attempt and the flag read
+  // once at the end; a failed attempt's outputs are recomputed.
+  double damp = 0.0;
+  for (int attempt = 0; attempt <= kMaxRetries; ++attempt) {
+    gptq_status s;
+    if ((s = enqueue_factor(S, n, d, p->percdamp, p->act_order, attempt, q.R,
+                            q.perm, q.dead, q.f, st)) != GPTQ_OK)
       return s;
-    Ru = q.R;
-    pu = q.perm;
-    du = q.dead;
+    if ((s = enqueue_columns(W, w_dtype, m, d, ldw, p, q.R, q.perm, q.dead, q,
+                             qweight, scales, zeros, g_idx, w_hat, st)) != GPTQ_OK)
+      return s;
+    bool ok = false;
+    if ((s = read_factor_outcome(q.f, st, &ok, &damp)) != GPTQ_OK) return s;
+    if (ok) return GPTQ_OK;
   }
-  const int64_t gsize = p->group_size;
-  // whole-row grid on the original row, before dead columns are zeroed
-  if (gsize == -1 &&
-      (s = launch_fit_rows(W, w_dtype, m, d, ldw, p->bits, q.scalesP, q.zerosP, st)) != GPTQ_OK)
-    return s;
-  if ((s = launch_init_work(W, w_dtype, m, d, ldw, pu, du, q.WT, q.pinv, st)) != GPTQ_OK)
-    return s;
-  const int bi = internal_block(d, p);
-  if ((s = launch_rbt(Ru, d, bi, q.RbT, st)) != GPTQ_OK) return s;
-  for (int64_t i0 = 0; i0 < d; i0 += bi) {
-    const int bw = static_cast<int>(std::min<int64_t>(bi, d - i0));
-    if ((s = launch_chain(q.WT, m, d, q.RbT, i0, bw, bi, p->bits, gsize,
-                          q.scalesP, q.zerosP, q.codesP, q.E, st)) != GPTQ_OK)
-      return s;
-    if ((s = launch_lazy_update(q.WT, m, d, Ru, i0, bw, q.E, st)) != GPTQ_OK)
-      return s;
-  }
-  return launch_outputs(m, d, p->bits, static_cast<int>(gsize), q.codesP,
-                        q.scalesP, q.zerosP, q.pinv, q.codesO, qweight, scales,
-                        zeros, g_idx, w_hat, st);
+  return GPTQ_ERR_NOT_SPD;
 }
 
 }  // extern "C"

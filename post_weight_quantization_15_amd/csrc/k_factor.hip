@@ -31,6 +31,8 @@ namespace {
 
 constexpr int kNb = 64;          // diagonal block / panel width
 constexpr int kGroup = 4;        // blocks per trailing update (k = 256)
+constexpr int64_t kCUs = 256;     // MI355X compute units
+constexpr int64_t kBgTiles = 3;   // deferred trailing tiles per idle workgroup
 constexpr double kEpsFloor = 1.1920928955078125e-07;   // 2^-23
 
 // ---------------------------------------------------------------------------
@@ -147,7 +149,10 @@ constexpr int kWp = kNb + 2;     // LDS pitch of the U / W arrays (16-B rows)
 // group's columns, every wave factors the 64 x 4 panel in registers (lane =
 // row; pivots from the right: U_cc = sqrt(A_cc), U_ic = A_ic / U_cc, then
 // the group's remaining columns lose U_:c U_c'c) and applies the rank-4
-// update A_ij -= sum_{c in G} U_ic U_jc to its columns j < g0.
+// update A_ij -= sum_{c in G} U_ic U_jc to its columns j < g0: at once to
+// its column in the next group (the only one the next barrier waits for),
+// the others during the next group's pivot chain.  Each column receives the
+// groups' updates in the same order either way.
 //
 // W_KK = U_KK^-1 (R's diagonal block, R = U^-1): the four 16 x 16 diagonal
 // blocks by back substitution, then W_12 = -W_11 U_12 W_22 at sizes 16 and
@@ -160,10 +165,23 @@ struct DiagLds {
   double Tl[32][34];
 };
 
-// Factor and invert the diagonal block into L.Us (U, upper, identity-padded)
-// and L.Wl (W = U^-1); returns true when a pivot was not positive.
-__device__ inline bool diag_factor(const double* __restrict__ H, int64_t d,
-                                   int64_t k0, int nbk, DiagLds& L) {
+// Stages the diagonal block [k0, k0 + nbk) of H in L.Us (upper part, the
+// rest identity) and clears L.Wl.
+__device__ inline void diag_load(const double* __restrict__ H, int64_t d,
+                                 int64_t k0, int nbk, DiagLds& L) {
+  for (int e = threadIdx.x; e < kNb * kNb; e += 256) {
+    const int r = e >> 6, c = e & 63;
+    double v = (r == c) ? 1.0 : 0.0;
+    if (r < nbk && c < nbk && r <= c) v = H[(k0 + r) * d + k0 + c];
+    L.Us[r][c] = v;
+    L.Wl[r][c] = 0.0;
+  }
+}
+
+// Factors and inverts the block staged in L.Us (upper triangle read; L.Wl
+// cleared) into L.Us (U, upper) and L.Wl (W = U^-1); returns true when a
+// pivot was not positive.
+__device__ inline bool diag_factor(DiagLds& L) {
   static_assert(kNb == 64, "thread/element split assumes 64 columns");
   auto& Us = L.Us;
   auto& Wl = L.Wl;
@@ -172,40 +190,71 @@ __device__ inline bool diag_factor(const double* __restrict__ H, int64_t d,
   auto& Tl = L.Tl;
   const int t = threadIdx.x;
   const int w = t >> 6, i = t & 63;
-  for (int e = t; e < kNb * kNb; e += 256) {
-    const int r = e >> 6, c = e & 63;
-    double v = (r == c) ? 1.0 : 0.0;
-    if (r < nbk && c < nbk && r <= c) v = H[(k0 + r) * d + k0 + c];
-    Us[r][c] = v;
-    Wl[r][c] = 0.0;
-  }
   __syncthreads();
   double a[16];
 #pragma unroll
   for (int u = 0; u < 16; ++u) a[u] = Us[i][w + 4 * u];
   __syncthreads();
-  bool bad = false;
+  double ok = 1.0;        // -1 once a pivot was not positive (or NaN)
+  double Up[4];           // previous group's U[i][g0 + cc] (deferred updates)
 #pragma unroll
   for (int g = 15; g >= 0; --g) {
     const int g0 = 4 * g;
     pan[g & 1][w][i] = a[g];             // column g0 + w
     __syncthreads();
-    double P[4], Uc[4];
+    // P[cc]: this lane's row of the group's columns.  q[r][cc]: the group's
+    // 4 x 4 diagonal block and qn[cc]: row g0 - 4 + w (the row of this
+    // wave's column in the next group), both the same in every lane of the
+    // wave (broadcast LDS reads), so the pivots and the next group's column
+    // need no cross-lane moves.
+    double P[4], Uc[4], q[4][4], qn[4];
 #pragma unroll
-    for (int cc = 0; cc < 4; ++cc) P[cc] = pan[g & 1][cc][i];
+    for (int cc = 0; cc < 4; ++cc) {
+      P[cc] = pan[g & 1][cc][i];
+#pragma unroll
+      for (int r = 0; r <= cc; ++r) q[r][cc] = pan[g & 1][cc][g0 + r];
+      qn[cc] = g > 0 ? pan[g & 1][cc][g0 - 4 + w] : 0.0;
+    }
+    // the previous group's update of this wave's other columns, deferred to
+    // here so that it overlaps this group's pivot chain
+    if (g < 15) {
+#pragma unroll
+      for (int u = g - 1; u >= 0; --u) {
+        const int jr = w + 4 * u;
+        const double2 u01 = *reinterpret_cast<const double2*>(&Us[jr][g0 + 4]);
+        const double2 u23 = *reinterpret_cast<const double2*>(&Us[jr][g0 + 6]);
+        double v = a[u];
+        v = fma(-Up[0], u01.x, v);
+        v = fma(-Up[1], u01.y, v);
+        v = fma(-Up[2], u23.x, v);
+        v = fma(-Up[3], u23.y, v);
+        a[u] = v;
+      }
+    }
+    double un[4], rsw[4];
 #pragma unroll
     for (int cc = 3; cc >= 0; --cc) {
-      const int c = g0 + cc;
-      double p = read_lane(P[cc], c);
-      const bool b = !(p > 0.0);
-      bad |= b;
-      p = b ? 1.0 : p;
+      // a pivot that is not positive leaves non-finite values behind; the
+      // flag discards the whole factor then
+      const double p = q[cc][cc];
+      ok = fmin(ok, (p > 0.0) ? p : -1.0);
       const double rs = rsqrt_refined(p);
-      Uc[cc] = (i < c) ? P[cc] * rs : (i == c ? p * rs : 0.0);
-      if (t == 0) rsl[c] = rs;
+      rsw[cc] = rs;
+      // rows below the pivot (i > c) carry values that are never read: the
+      // lower triangle of U is not used
+      Uc[cc] = P[cc] * rs;
+      // U[g0 + r][c] and U[g0 - 4 + w][c] as their own lanes compute them
+      double uq[4];
 #pragma unroll
-      for (int c2 = cc - 1; c2 >= 0; --c2)
-        P[c2] = fma(-Uc[cc], read_lane(Uc[cc], g0 + c2), P[c2]);
+      for (int r = 0; r < cc; ++r) uq[r] = q[r][cc] * rs;
+      un[cc] = qn[cc] * rs;
+#pragma unroll
+      for (int c2 = cc - 1; c2 >= 0; --c2) {
+        P[c2] = fma(-Uc[cc], uq[c2], P[c2]);
+        qn[c2] = fma(-un[cc], uq[c2], qn[c2]);
+#pragma unroll
+        for (int r = 0; r <= c2; ++r) q[r][c2] = fma(-uq[r], uq[c2], q[r][c2]);
+      }
     }
     // every wave writes the same values; a wave reads back only after its
     // own writes (LDS operations of one wave complete in order)
@@ -213,20 +262,26 @@ __device__ inline bool diag_factor(const double* __restrict__ H, int64_t d,
     *reinterpret_cast<double2*>(&Us[i][g0 + 2]) = double2{Uc[2], Uc[3]};
     __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
     __builtin_amdgcn_wave_barrier();
+    if (g > 0) {                         // the next group's column now
+      double v = a[g - 1];
+      v = fma(-Uc[0], un[0], v);
+      v = fma(-Uc[1], un[1], v);
+      v = fma(-Uc[2], un[2], v);
+      v = fma(-Uc[3], un[3], v);
+      a[g - 1] = v;
+    }
 #pragma unroll
-    for (int u = g - 1; u >= 0; --u) {   // the next group's column first
-      const int jr = w + 4 * u;
-      const double2 u01 = *reinterpret_cast<const double2*>(&Us[jr][g0]);
-      const double2 u23 = *reinterpret_cast<const double2*>(&Us[jr][g0 + 2]);
-      double v = a[u];
-      v = fma(-Uc[0], u01.x, v);
-      v = fma(-Uc[1], u01.y, v);
-      v = fma(-Uc[2], u23.x, v);
-      v = fma(-Uc[3], u23.y, v);
-      a[u] = v;
+    for (int cc = 0; cc < 4; ++cc) Up[cc] = Uc[cc];
+    if (t < 4) {
+      double v = rsw[0];
+      v = (t == 1) ? rsw[1] : v;
+      v = (t == 2) ? rsw[2] : v;
+      v = (t == 3) ? rsw[3] : v;
+      rsl[g0 + t] = v;
     }
   }
   __syncthreads();
+  const bool bad = !(ok > 0.0);
   const int lane = i, lr = lane & 15, lk = lane >> 4;
   // 16 x 16 diagonal blocks of W: wave w, lanes 0..15 solve one column each
   if (lane < 16) {
@@ -302,7 +357,8 @@ __global__ __launch_bounds__(256) void chol_diag_kernel(
     double* __restrict__ H, double* __restrict__ R, int64_t d, int64_t k0,
     int nbk, int* __restrict__ flag) {
   __shared__ __align__(16) DiagLds L;
-  const bool bad = diag_factor(H, d, k0, nbk, L);
+  diag_load(H, d, k0, nbk, L);
+  const bool bad = diag_factor(L);
   diag_store(R, d, k0, nbk, bad, L, flag);
 }
 
@@ -321,11 +377,22 @@ __global__ __launch_bounds__(256) void chol_diag_kernel(
 constexpr int kKc = 32;            // k chunk
 constexpr int kLp = kKc + 2;       // LDS pitch (doubles)
 
+struct GemmLds {
+  double As[64][kLp];
+  double Bs[64][kLp];
+};
+
+// One staging area per kernel, shared by every tile_gemm instantiation in it.
+__device__ inline GemmLds& gemm_lds() {
+  __shared__ GemmLds g;
+  return g;
+}
+
 template <bool B_KC, class FA, class FB>
 __device__ inline void tile_gemm(int64_t kbeg, int64_t kend, FA fa, FB fb,
                                  f64x4 acc[2][2]) {
-  __shared__ double As[64][kLp];
-  __shared__ double Bs[64][kLp];
+  auto& As = gemm_lds().As;
+  auto& Bs = gemm_lds().Bs;
   const int t = threadIdx.x;
   const int lane = t & 63, wv = t >> 6;
   const int wr = (wv >> 1) * 32, wc = (wv & 1) * 32;
@@ -398,12 +465,14 @@ __device__ inline void zero_acc(f64x4 acc[2][2]) {
     for (int g = 0; g < 2; ++g) acc[h][g] = f64x4{0.0, 0.0, 0.0, 0.0};
 }
 
-// Step 3: A[i][j] -= sum_c P[i][c] P[j][c] over the upper 64x64 tiles of
-// [0, k0)^2 whose tile column is tj0 + blockIdx.x, P = H[:, k0:k0+nbk].
+// The trailing update after a group: A[i][j] -= sum_c P[i][c] P[j][c] over
+// the upper 64x64 tiles of [0, k0)^2 in tile columns tj0.., P = H[:,
+// k0:k0+nbk], except the last diagonal tile (the group's step kernels
+// updated and factored it).
 __global__ __launch_bounds__(256) void syrk_update_kernel(
     double* __restrict__ H, int64_t d, int64_t k0, int nbk, int64_t tj0) {
   const int64_t ti = blockIdx.y, tj = tj0 + blockIdx.x;
-  if (ti > tj) return;
+  if (ti > tj || (ti == tj && (ti + 1) * 64 >= k0)) return;
   const int64_t I0 = ti * 64, J0 = tj * 64;
   const double* P = H + k0;
   auto fa = [&](int ii, int64_t k) -> double {
@@ -423,27 +492,213 @@ __global__ __launch_bounds__(256) void syrk_update_kernel(
   });
 }
 
-// Step 2: U_iK = A_iK W_KK^T for the rows i < k0, 64 rows per workgroup,
-// in place (a workgroup reads all of its rows' panel before writing it).
-__global__ __launch_bounds__(256) void chol_panel_kernel(
-    double* __restrict__ H, const double* __restrict__ R, int64_t d,
-    int64_t k0, int nbk) {
+// One block K = [k0, k0 + nbk) of a group of blocks [kg, kend), one
+// workgroup per 64-row tile i above it (I0 < k0).  The group's blocks are
+// taken from the bottom; P = [kp, kp + nbp) is the one before K (kp < 0 for
+// the group's first block).  Every row tile:
+//   A_iC -= U_iP U_CP^T   for the group's column tiles C = K and the ones to
+//                         its left down to kg (C above the diagonal): P's
+//                         share, one block late, so that these updates never
+//                         wait on another workgroup;
+//   U_iK  = A_iK W_KK^T   (the panel; W_KK from the diagonal factor).
+// The row tiles J in [kg - 64, k0) -- the group's later blocks and the next
+// group's first one -- also take K's share of their own diagonal tile,
+// A_JJ -= U_JK U_JK^T, and the one right above K (J = k0 - 64, whose block
+// comes next) then factors and inverts it; the trailing update after the
+// group leaves that tile out.  A_iK and U_iK stay in LDS between the steps.
+// Workgroups past the row tiles apply part of the previous group's trailing
+// update to the tiles this group never reads (see trailing_tiles).
+// 64 x 64 products with k <= 64 in one LDS stage, for the step kernel: A(i,
+// k) and B(j, k) (B k-contiguous) both [64][kWp], zero past the k range.
+// Thread t holds operand elements e = t + 256u (u < 16) at (e / 64, e % 64),
+// which keeps the global loads row-contiguous.
+struct Tile64Lds {
+  double As[kNb][kWp];
+  double Bs[kNb][kWp];
+};
+
+__device__ inline Tile64Lds& tile64_lds() {
+  __shared__ __align__(16) Tile64Lds g;
+  return g;
+}
+
+template <class F>
+__device__ inline void load64(F f, double r[16]) {
+#pragma unroll
+  for (int u = 0; u < 16; ++u) {
+    const int e = threadIdx.x + 256 * u;
+    r[u] = f(e >> 6, e & 63);
+  }
+}
+
+__device__ inline void stage64(const double r[16], double (&S)[kNb][kWp]) {
+#pragma unroll
+  for (int u = 0; u < 16; ++u) {
+    const int e = threadIdx.x + 256 * u;
+    S[e >> 6][e & 63] = r[u];
+  }
+}
+
+// acc += A B^T over k < 64 (same output map as tile_gemm / tile_store).
+__device__ inline void mma64(const double (&A)[kNb][kWp], const double (&B)[kNb][kWp],
+                             f64x4 acc[2][2]) {
+  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+  const int wr = (wv >> 1) * 32, wc = (wv & 1) * 32;
+  const int lr = lane & 15, lk = lane >> 4;
+#pragma unroll
+  for (int ks = 0; ks < kNb; ks += 4) {
+    const double a0 = A[wr + lr][ks + lk], a1 = A[wr + 16 + lr][ks + lk];
+    const double b0 = B[wc + lr][ks + lk], b1 = B[wc + 16 + lr][ks + lk];
+    acc[0][0] = __builtin_amdgcn_mfma_f64_16x16x4f64(a0, b0, acc[0][0], 0, 0, 0);
+    acc[0][1] = __builtin_amdgcn_mfma_f64_16x16x4f64(a0, b1, acc[0][1], 0, 0, 0);
+    acc[1][0] = __builtin_amdgcn_mfma_f64_16x16x4f64(a1, b0, acc[1][0], 0, 0, 0);
+    acc[1][1] = __builtin_amdgcn_mfma_f64_16x16x4f64(a1, b1, acc[1][1], 0, 0, 0);
+  }
+}
+
+// Loads a 64 x 64 tile in the product output map (see tile_store).
+template <class F>
+__device__ inline void load_out(F f, double r[16]) {
+  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+  const int wr = (wv >> 1) * 32, wc = (wv & 1) * 32;
+#pragma unroll
+  for (int h = 0; h < 2; ++h)
+#pragma unroll
+    for (int g = 0; g < 2; ++g)
+#pragma unroll
+      for (int v = 0; v < 4; ++v)
+        r[(h * 2 + g) * 4 + v] = f(wr + 16 * h + (lane >> 4) + 4 * v, wc + 16 * g + (lane & 15));
+}
+
+// The previous group's trailing update on the tiles no step of this group
+// touches, A_ij -= P_i P_j^T with P = H[:, bk:bk+bK] (bK <= 256): upper
+// tiles numbered column-major, L = tj (tj + 1) / 2 + ti, this workgroup
+// taking L = t0 + b, t0 + b + nbg, ... below t0 + nt.
+__device__ inline void trailing_tiles(double* __restrict__ H, int64_t d,
+                                      int64_t bk, int bK, int64_t t0, int64_t nt,
+                                      int64_t b, int64_t nbg) {
+  auto& T = tile64_lds();
+  for (int64_t q = b; q < nt; q += nbg) {
+    const int64_t Lq = t0 + q;
+    int64_t tj = static_cast<int64_t>((sqrt(8.0 * double(Lq) + 1.0) - 1.0) * 0.5);
+    while (tj * (tj + 1) / 2 > Lq) --tj;
+    while ((tj + 1) * (tj + 2) / 2 <= Lq) ++tj;
+    const int64_t ti = Lq - tj * (tj + 1) / 2;
+    const double* Pi = H + ti * 64 * d + bk;
+    const double* Pj = H + tj * 64 * d + bk;
+    f64x4 acc[2][2];
+    zero_acc(acc);
+    double ra[16], rb[16];
+    auto fetch = [&](int kc) {
+      load64([&](int i, int k) { return kc + k < bK ? Pi[int64_t(i) * d + kc + k] : 0.0; }, ra);
+      load64([&](int j, int k) { return kc + k < bK ? Pj[int64_t(j) * d + kc + k] : 0.0; }, rb);
+    };
+    fetch(0);
+    for (int kc = 0; kc < bK; kc += 64) {
+      __syncthreads();                         // the previous chunk's products are done
+      stage64(ra, T.As);
+      stage64(rb, T.Bs);
+      __syncthreads();
+      if (kc + 64 < bK) fetch(kc + 64);
+      mma64(T.As, T.Bs, acc);
+    }
+    double* Dt = H + ti * 64 * d + tj * 64;
+    tile_store(acc, [&](int ii, int jj, double v) {
+      if (ti != tj || ii <= jj) Dt[int64_t(ii) * d + jj] -= v;
+    });
+  }
+}
+
+__global__ __launch_bounds__(256) void chol_step_kernel(
+    double* __restrict__ H, double* __restrict__ R, int64_t d, int64_t k0,
+    int nbk, int64_t kp, int nbp, int64_t kg, int* __restrict__ flag,
+    int64_t bk, int bK, int64_t t0, int64_t nt) {
+  __shared__ __align__(16) DiagLds L;
+  auto& T = tile64_lds();
+  const int64_t nrow = k0 / 64;
+  if (int64_t(blockIdx.x) >= nrow) {           // the chip's idle workgroups
+    trailing_tiles(H, d, bk, bK, t0, nt, blockIdx.x - nrow, gridDim.x - nrow);
+    return;
+  }
+  auto& At = L.Us;                 // A_iK, then (next block's tile) its U
+  auto& Pt = L.Wl;                 // U_iK, then (next block's tile) its W
   const int64_t I0 = int64_t(blockIdx.x) * 64;
+  const bool diag_later = I0 >= kg - kNb;     // a diagonal tile still to come
   const double* W = R + k0 * d + k0;
-  auto fa = [&](int ii, int64_t k) -> double {
-    const int64_t i = I0 + ii;
-    return i < k0 ? H[i * d + k0 + k] : 0.0;
-  };
-  auto fb = [&](int64_t k, int jj) -> double {   // B(k, j) = W[j][k], upper
-    return (jj < nbk && k >= jj) ? W[int64_t(jj) * d + k] : 0.0;
-  };
+  double* D = H + I0 * d + I0;
   f64x4 acc[2][2];
+  // every global operand of the chain is requested up front
+  double ra[16], rb[16], rw[16], rk[16], rd[16];
+  if (kp >= 0) {
+    load64([&](int i, int k) { return k < nbp ? H[(I0 + i) * d + kp + k] : 0.0; }, ra);
+    load64([&](int j, int k) {
+      return (j < nbk && k < nbp) ? H[(k0 + j) * d + kp + k] : 0.0;
+    }, rb);
+  }
+  load64([&](int j, int k) {                   // B(k, j) = W[j][k], upper
+    return (j < nbk && k < nbk && k >= j) ? W[int64_t(j) * d + k] : 0.0;
+  }, rw);
+  load_out([&](int i, int j) { return j < nbk ? H[(I0 + i) * d + k0 + j] : 0.0; }, rk);
+  if (diag_later)
+    load_out([&](int i, int j) { return i <= j ? D[int64_t(i) * d + j] : 0.0; }, rd);
+  // P's share: C = k0 first (into At), then C = k0 - 64, ... (in place)
+  if (kp >= 0) {
+    stage64(ra, T.As);
+    for (int64_t c = k0; c >= kg && c > I0; c -= 64) {
+      if (c != k0) {
+        load64([&](int j, int k) { return k < nbp ? H[(c + j) * d + kp + k] : 0.0; }, rb);
+        __syncthreads();                       // the previous product read T.Bs
+      }
+      stage64(rb, T.Bs);
+      __syncthreads();
+      zero_acc(acc);
+      mma64(T.As, T.Bs, acc);
+      if (c == k0) {
+        int q = 0;
+        tile_store(acc, [&](int ii, int jj, double v) { At[ii][jj] = rk[q++] - v; });
+      } else {
+        tile_store(acc, [&](int ii, int jj, double v) { H[(I0 + ii) * d + c + jj] -= v; });
+      }
+    }
+  } else {
+    zero_acc(acc);
+    int q = 0;
+    tile_store(acc, [&](int ii, int jj, double) { At[ii][jj] = rk[q++]; });
+  }
+  __syncthreads();                             // T.Bs free, At complete
+  stage64(rw, T.Bs);
+  __syncthreads();
   zero_acc(acc);
-  tile_gemm<true>(0, nbk, fa, fb, acc);
+  mma64(At, T.Bs, acc);
   tile_store(acc, [&](int ii, int jj, double v) {
-    const int64_t i = I0 + ii;
-    if (i < k0 && jj < nbk) H[i * d + k0 + jj] = v;
+    if (jj < nbk) H[(I0 + ii) * d + k0 + jj] = v;
+    Pt[ii][jj] = v;
   });
+  if (!diag_later) return;
+  __syncthreads();
+  zero_acc(acc);
+  mma64(Pt, Pt, acc);
+  if (I0 + kNb < k0) {
+    int q = 0;
+    tile_store(acc, [&](int ii, int jj, double v) {
+      const double x = rd[q++] - v;
+      if (ii <= jj) D[int64_t(ii) * d + jj] = x;
+    });
+    return;
+  }
+  // the next block's diagonal tile (64 wide: only the bottom block of the
+  // matrix is narrower, and it comes first)
+  __syncthreads();                             // every product read At / Pt
+  {
+    int q = 0;
+    tile_store(acc, [&](int ii, int jj, double v) {
+      At[ii][jj] = ii <= jj ? rd[q] - v : 0.0;
+      Pt[ii][jj] = 0.0;
+      ++q;
+    });
+  }
+  const bool bad = diag_factor(L);
+  diag_store(R, d, I0, kNb, bad, L, flag);
 }
 
 // ---------------------------------------------------------------------------
@@ -576,35 +831,79 @@ gptq_status launch_cholesky_upper(int64_t d, const FactorWs& f,
   zero_flag_kernel<<<1, 1, 0, st>>>(f.flag);
   GPTQ_CHECK_LAUNCH();
   // 64-column blocks, 64-aligned from the top (the bottom one absorbs
-  // d % 64), taken from the bottom in groups of kGroup.  Inside a group each
-  // block gets the contributions of the group's blocks below it only on its
-  // own column tile; the rest of the trailing matrix receives the whole
-  // group at once, one update with k = up to 64 kGroup.
+  // d % 64), taken from the bottom in groups of kGroup.  Inside a group the
+  // step kernels update only the group's own columns (and the diagonal tile
+  // of the block after it); the rest of the trailing matrix receives the
+  // whole group at once, one update with k = up to 64 kGroup.  Only the
+  // bottom block's diagonal factor has a launch of its own: each step kernel
+  // factors the next block's.
   int64_t k1 = d;
+  {
+    const int nb0 = static_cast<int>((d % kNb) ? (d % kNb) : kNb);
+    chol_diag_kernel<<<1, 256, 0, st>>>(f.H, f.R, d, d - nb0, nb0, f.flag);
+    GPTQ_CHECK_LAUNCH();
+  }
+  // the previous group's deferred trailing tiles: P = H[:, bk:bk+bK],
+  // upper tiles with tile column < defer_tj
+  int64_t bk = 0, defer_tj = 0;
+  int bK = 0;
   while (k1 > 0) {
     const int64_t kend = k1;
-    for (int x = 0; x < kGroup && k1 > 0; ++x) {
-      const int nbk = static_cast<int>((k1 % kNb) ? (k1 % kNb) : kNb);
-      const int64_t k0 = k1 - nbk;
-      if (x > 0) {
-        // A[i][j] -= U[i][k1:kend] U[j][k1:kend]^T for j in this block, i <= j
-        syrk_update_kernel<<<dim3(1, cdiv(k1, 64)), 256, 0, st>>>(
-            f.H, d, k1, static_cast<int>(kend - k1), k0 / 64);
-        GPTQ_CHECK_LAUNCH();
-      }
-      chol_diag_kernel<<<1, 256, 0, st>>>(f.H, f.R, d, k0, nbk, f.flag);
-      GPTQ_CHECK_LAUNCH();
-      if (k0 > 0) {
-        chol_panel_kernel<<<cdiv(k0, 64), 256, 0, st>>>(f.H, f.R, d, k0, nbk);
-        GPTQ_CHECK_LAUNCH();
-      }
-      k1 = k0;
+    int64_t bk0[kGroup];
+    int bnb[kGroup];
+    int nb = 0;
+    for (int64_t k = k1; nb < kGroup && k > 0; ++nb) {
+      bnb[nb] = static_cast<int>((k % kNb) ? (k % kNb) : kNb);
+      bk0[nb] = k - bnb[nb];
+      k = bk0[nb];
     }
-    if (k1 > 0) {
-      const unsigned nt = cdiv(k1, 64);
-      syrk_update_kernel<<<dim3(nt, nt), 256, 0, st>>>(
-          f.H, d, k1, static_cast<int>(kend - k1), 0);
+    const int64_t kg = bk0[nb - 1];
+    int nl = 0;
+    while (nl < nb && bk0[nl] > 0) ++nl;
+    const int64_t ntask = defer_tj * (defer_tj + 1) / 2;
+    // deferred tiles shared out in proportion to each launch's idle
+    // workgroups (every launch has some: see the cap below)
+    int64_t idle[kGroup], idle_sum = 0;
+    for (int x = 0; x < nl; ++x) {
+      idle[x] = std::max<int64_t>(0, kCUs - bk0[x] / 64);
+      idle_sum += idle[x];
+    }
+    int64_t tdone = 0, idle_acc = 0;
+    for (int x = 0; x < nl; ++x) {
+      const int64_t nrow = bk0[x] / 64;
+      idle_acc += idle[x];
+      const int64_t ta = tdone;
+      const int64_t tb = idle_sum > 0 ? ntask * idle_acc / idle_sum : 0;
+      tdone = tb;
+      const int64_t nbg = std::min<int64_t>(tb - ta, idle[x]);
+      chol_step_kernel<<<static_cast<unsigned>(nrow + nbg), 256, 0, st>>>(
+          f.H, f.R, d, bk0[x], bnb[x], x > 0 ? bk0[x - 1] : -1, x > 0 ? bnb[x - 1] : 0,
+          kg, f.flag, bk, bK, ta, tb - ta);
       GPTQ_CHECK_LAUNCH();
+    }
+    // deferred work must have found a launch: it exists only when the next
+    // group has all of its blocks below row 0
+    if (ntask > 0 && nl == 0) return GPTQ_ERR_HIP;
+    k1 = kg;
+    defer_tj = 0;
+    if (k1 > kNb) {
+      // now: the tile columns the next group reads (its own columns and the
+      // first block of the one after); the rest rides along with the next
+      // group's step kernels
+      const int64_t nt = cdiv(k1, 64);
+      // deferred tiles must fit the next group's idle workgroups, at most
+      // kBgTiles each: its launches have k1 / 64 - x - 1 row tiles
+      int64_t cap = 0;
+      for (int x = 0; x < kGroup; ++x)
+        cap += kBgTiles * std::max<int64_t>(0, kCUs - (k1 / 64 - x - 1));
+      int64_t tj0 = std::max<int64_t>(0, nt - (kGroup + 1));
+      while (tj0 > 0 && tj0 * (tj0 + 1) / 2 > cap) --tj0;
+      syrk_update_kernel<<<dim3(static_cast<unsigned>(nt - tj0), static_cast<unsigned>(nt)), 256, 0, st>>>(
+          f.H, d, k1, static_cast<int>(kend - k1), tj0);
+      GPTQ_CHECK_LAUNCH();
+      defer_tj = tj0;
+      bk = k1;
+      bK = static_cast<int>(kend - k1);
     }
   }
   return GPTQ_OK;

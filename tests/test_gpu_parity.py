@@ -242,6 +242,49 @@ def test_shared_hessian_reuses_factor(dev):
             assert torch.equal(a[k], b[k]), (nm, k)
 
 
+def indefinite_s(d, n, lam_min, seed):
+    """S = (n/2) H with H = Q diag(lam) Q^T, one eigenvalue lam_min < 0 and
+    the rest in [1, 2]: the damping retries until it exceeds -lam_min."""
+    rng = np.random.default_rng(seed)
+    Q, _ = np.linalg.qr(rng.standard_normal((d, d)))
+    lam = np.linspace(1.0, 2.0, d)
+    lam[0] = lam_min
+    H = (Q * lam) @ Q.T
+    H = 0.5 * (H + H.T)
+    return (0.5 * n * H).astype(np.float32)
+
+
+def test_layer_retry_then_success(dev):
+    """The layer's internal factor goes through failed damping attempts
+    (0.015 and 0.15 < 0.5) before succeeding; the result equals quantizing
+    with the factor from the separate entry point, whose damping matches the
+    oracle's retry."""
+    d, n, m = 96, 1000, 48
+    S32 = indefinite_s(d, n, -0.5, 21)
+    S = torch.from_numpy(S32).to(dev)
+    params = dict(bits=4, group_size=32, blocksize=32, percdamp=0.01, act_order=True)
+    R, perm, dead, damp = gq.gptq_cholesky_inverse(S, n, params["percdamp"], True)
+    H, _, _, damp_o = orc.prepare(S32.astype(np.float64), n, params["percdamp"], True)
+    _, damp_o = orc.factor(H, damp_o)
+    assert damp_o > 0.5 and math.isclose(damp, damp_o, rel_tol=1e-6), (damp, damp_o)
+    Wg = synth.normal_weight(m, d, 0.02, 21, "retry/W", "cpu").to(dev)
+    a = gq.gptq_quantize_layer(Wg, S, n, want_w_hat=True, **params)
+    b = gq.gptq_quantize_layer(Wg, None, 0, R=R, perm=perm, dead=dead,
+                               want_w_hat=True, **params)
+    for k in a:
+        assert torch.equal(a[k], b[k]), k
+
+
+def test_layer_not_spd(dev):
+    d, n = 40, 100
+    S = torch.from_numpy(indefinite_s(d, n, -1e9, 22)).to(dev)
+    W = torch.randn(8, d, device=dev)
+    with pytest.raises(gq.GPTQError) as ei:
+        gq.gptq_quantize_layer(W, S, n, bits=4, group_size=-1, blocksize=128,
+                               percdamp=0.01, act_order=False)
+    assert ei.value.status == gq.GPTQ_ERR_NOT_SPD
+
+
 def test_quantize_deterministic(dev):
     W, X, params = layer_case("attn")
     a, _ = run_gpu_layer(W, X, params, dev)
