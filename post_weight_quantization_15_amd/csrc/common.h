@@ -94,11 +94,18 @@ gptq_status launch_rbt(const float* R, int64_t d, int bi, float* RL,
                        hipStream_t st);
 // Block [i0, i0 + bw) of the column loop (bw <= bi <= 128).  scalesP/zerosP
 // are [n_g][m] (processing-group major); for group_size -1 row 0 holds the
-// row grids.  Writes the block's codes and its residuals E [bw][m].
+// row grids.  Writes the block's codes and its residuals E [bw][m].  The
+// block belongs to a lazy batch starting at column sb0 (a multiple of 32
+// columns before i0) whose earlier blocks' residuals Esb [i0 - sb0][m] have
+// not been applied to WT yet: the kernel applies them to its own columns
+// first (R: fp32 [d][d]).
 gptq_status launch_chain(float* WT, int64_t m, int64_t d, const float* RL,
                          int64_t i0, int bw, int bi, int bits, int64_t gsize,
                          float* scalesP, uint8_t* zerosP, uint8_t* codesP,
-                         float* E, hipStream_t st);
+                         float* E, const float* R, int64_t sb0, const float* Esb,
+                         hipStream_t st);
+// WT[:, i0 + bw:] -= E^T R[i0:i0 + bw, i0 + bw:] for a lazy batch of bw <= 512
+// columns; E [bw][m] with room for its rows padded to the product's k steps.
 gptq_status launch_lazy_update(float* WT, int64_t m, int64_t d, const float* R,
                                int64_t i0, int bw, float* E,
                                hipStream_t st);

@@ -10,6 +10,7 @@ namespace {
 
 constexpr int64_t kMaxDim = 65535;   // grid.y limit of the per-row launches
 constexpr int kChainMaxBlock = 128;
+constexpr int kLazyBatch = 2;        // chain blocks per lazy (far) update
 constexpr int kMaxRetries = 5;
 
 bool valid_dtype(gptq_dtype t) { return t == GPTQ_BF16 || t == GPTQ_F32; }
@@ -68,7 +69,7 @@ QuantWs carve_quant_ws(Carver& c, int64_t m, int64_t d, const gptq_params* p,
   const int bi = internal_block(d, p);
   const int64_t nblk = (d + bi - 1) / bi;
   q.WT = c.take<float>(size_t(d) * size_t(m));
-  q.E = c.take<float>(size_t(kChainMaxBlock) * size_t(m));
+  q.E = c.take<float>(size_t(kLazyBatch) * size_t(kChainMaxBlock) * size_t(m));
   q.codesP = c.take<uint8_t>(size_t(d) * size_t(m));
   q.codesO = c.take<uint8_t>(size_t(d) * size_t(m));
   q.scalesP = c.take<float>(size_t(ng) * size_t(m));
@@ -148,12 +149,25 @@ gptq_status enqueue_columns(const void* W, gptq_dtype w_dtype, int64_t m,
     return s;
   const int bi = internal_block(d, p);
   if ((s = launch_rbt(Ru, d, bi, q.RbT, st)) != GPTQ_OK) return s;
-  for (int64_t i0 = 0; i0 < d; i0 += bi) {
-    const int bw = static_cast<int>(std::min<int64_t>(bi, d - i0));
-    if ((s = launch_chain(q.WT, m, d, q.RbT, i0, bw, bi, p->bits, gsize,
-                          q.scalesP, q.zerosP, q.codesP, q.E, st)) != GPTQ_OK)
-      return s;
-    if ((s = launch_lazy_update(q.WT, m, d, Ru, i0, bw, q.E, st)) != GPTQ_OK)
+  // Lazy batches of nb blocks: each block's chain first applies the batch's
+  // earlier residuals to its own columns, and one update per batch carries
+  // the whole batch to the columns after it (the same sums regrouped, as
+  // lazy batching itself is).  Batches need full 128-column blocks and no
+  // group reaching past its block, whose fit would read columns of the
+  // batch that have not received the batch's residuals yet.
+  const bool batch = bi == kChainMaxBlock && (gsize == -1 || bi % gsize == 0);
+  const int nb = batch ? kLazyBatch : 1;
+  for (int64_t s0 = 0; s0 < d; s0 += int64_t(nb) * bi) {
+    int64_t i0 = s0;
+    for (int j = 0; j < nb && i0 < d; ++j, i0 += bi) {
+      const int bw = static_cast<int>(std::min<int64_t>(bi, d - i0));
+      if ((s = launch_chain(q.WT, m, d, q.RbT, i0, bw, bi, p->bits, gsize,
+                            q.scalesP, q.zerosP, q.codesP, q.E + (i0 - s0) * m, Ru,
+                            s0, q.E, st)) != GPTQ_OK)
+        return s;
+    }
+    const int kw = static_cast<int>(std::min<int64_t>(int64_t(nb) * bi, d - s0));
+    if ((s = launch_lazy_update(q.WT, m, d, Ru, s0, kw, q.E, st)) != GPTQ_OK)
       return s;
   }
   return launch_outputs(m, d, p->bits, static_cast<int>(gsize), q.codesP,

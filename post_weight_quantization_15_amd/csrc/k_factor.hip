@@ -32,7 +32,7 @@ namespace {
 constexpr int kNb = 64;          // diagonal block / panel width
 constexpr int kGroup = 4;        // blocks per trailing update (k = 256)
 constexpr int64_t kCUs = 256;     // MI355X compute units
-constexpr int64_t kBgTiles = 3;   // deferred trailing tiles per idle workgroup
+constexpr int64_t kBgTiles = 2;   // deferred trailing tiles per idle workgroup
 constexpr double kEpsFloor = 1.1920928955078125e-07;   // 2^-23
 
 // ---------------------------------------------------------------------------
@@ -181,7 +181,7 @@ __device__ inline void diag_load(const double* __restrict__ H, int64_t d,
 // Factors and inverts the block staged in L.Us (upper triangle read; L.Wl
 // cleared) into L.Us (U, upper) and L.Wl (W = U^-1); returns true when a
 // pivot was not positive.
-__device__ inline bool diag_factor(DiagLds& L) {
+__device__ __attribute__((always_inline)) inline bool diag_factor(DiagLds& L) {
   static_assert(kNb == 64, "thread/element split assumes 64 columns");
   auto& Us = L.Us;
   auto& Wl = L.Wl;
@@ -215,20 +215,13 @@ __device__ inline bool diag_factor(DiagLds& L) {
       for (int r = 0; r <= cc; ++r) q[r][cc] = pan[g & 1][cc][g0 + r];
       qn[cc] = g > 0 ? pan[g & 1][cc][g0 - 4 + w] : 0.0;
     }
-    // the previous group's update of this wave's other columns, deferred to
-    // here so that it overlaps this group's pivot chain
+    double2 ud[15][2];     // rows w + 4u of the previous group's U columns
     if (g < 15) {
 #pragma unroll
       for (int u = g - 1; u >= 0; --u) {
         const int jr = w + 4 * u;
-        const double2 u01 = *reinterpret_cast<const double2*>(&Us[jr][g0 + 4]);
-        const double2 u23 = *reinterpret_cast<const double2*>(&Us[jr][g0 + 6]);
-        double v = a[u];
-        v = fma(-Up[0], u01.x, v);
-        v = fma(-Up[1], u01.y, v);
-        v = fma(-Up[2], u23.x, v);
-        v = fma(-Up[3], u23.y, v);
-        a[u] = v;
+        ud[u][0] = *reinterpret_cast<const double2*>(&Us[jr][g0 + 4]);
+        ud[u][1] = *reinterpret_cast<const double2*>(&Us[jr][g0 + 6]);
       }
     }
     double un[4], rsw[4];
@@ -254,6 +247,20 @@ __device__ inline bool diag_factor(DiagLds& L) {
         qn[c2] = fma(-un[cc], uq[c2], qn[c2]);
 #pragma unroll
         for (int r = 0; r <= c2; ++r) q[r][c2] = fma(-uq[r], uq[c2], q[r][c2]);
+      }
+    }
+    // the previous group's update of this wave's other columns, deferred to
+    // this group: its operands were read with the pivot block, its FMAs fill
+    // the pivot chain's latency
+    if (g < 15) {
+#pragma unroll
+      for (int u = g - 1; u >= 0; --u) {
+        double v = a[u];
+        v = fma(-Up[0], ud[u][0].x, v);
+        v = fma(-Up[1], ud[u][0].y, v);
+        v = fma(-Up[2], ud[u][1].x, v);
+        v = fma(-Up[3], ud[u][1].y, v);
+        a[u] = v;
       }
     }
     // every wave writes the same values; a wave reads back only after its

@@ -167,7 +167,8 @@ __global__ __launch_bounds__(256) void chain_kernel(
     const float* __restrict__ WT, int64_t m, int64_t d, const float* __restrict__ RL,
     int64_t i0, int bw, int bi, float maxq, int64_t gsize,
     float* __restrict__ scalesP, uint8_t* __restrict__ zerosP,
-    uint8_t* __restrict__ codesP, float* __restrict__ E) {
+    uint8_t* __restrict__ codesP, float* __restrict__ E,
+    const float* __restrict__ R, int64_t sb0, int kn, const float* __restrict__ Esb) {
   __shared__ __attribute__((aligned(16))) float rl[kB * kB];
   __shared__ float tile[kB][kTp];
   __shared__ uint8_t ctile[kB][kChainRows];
@@ -210,6 +211,50 @@ __global__ __launch_bounds__(256) void chain_kernel(
     for (int u = 0; u < 8; ++u) tile[c][8 * h + u] = v[u];
   }
   __syncthreads();
+  if (kn > 0) {
+    // the earlier blocks of this lazy batch, not yet applied to WT:
+    // tile[c][rr] -= sum_{k < kn} Esb[k][r0 + rr] R[sb0 + k][i0 + c]
+    // (wave wv: columns 32 wv .. 32 wv + 31 as two 16 x 16 MFMA blocks)
+    const int wv = tid >> 6, l = tid & 63, lr = l & 15, lk = l >> 4;
+    const float* Ea = Esb + min(r0 + lr, m - 1);
+    const float* Rb0 = R + sb0 * d + min(i0 + 32 * wv + lr, d - 1);
+    const float* Rb1 = R + sb0 * d + min(i0 + 32 * wv + 16 + lr, d - 1);
+    f32x4 acc0 = {0.f, 0.f, 0.f, 0.f}, acc1 = {0.f, 0.f, 0.f, 0.f};
+    // 32 k per batch (kn is a multiple of 32), the next batch's loads in
+    // flight during the current batch's products
+    float a[2][8], b0[2][8], b1[2][8];
+    auto fetch = [&](int buf, int k0) {
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        const int64_t k = k0 + 4 * u + lk;
+        a[buf][u] = Ea[k * m];
+        b0[buf][u] = Rb0[k * d];
+        b1[buf][u] = Rb1[k * d];
+      }
+    };
+    auto mma = [&](int buf) {
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        acc0 = __builtin_amdgcn_mfma_f32_16x16x4f32(a[buf][u], b0[buf][u], acc0, 0, 0, 0);
+        acc1 = __builtin_amdgcn_mfma_f32_16x16x4f32(a[buf][u], b1[buf][u], acc1, 0, 0, 0);
+      }
+    };
+    fetch(0, 0);
+    for (int k0 = 0; k0 < kn; k0 += 64) {
+      if (k0 + 32 < kn) fetch(1, k0 + 32);
+      mma(0);
+      if (k0 + 32 >= kn) break;
+      if (k0 + 64 < kn) fetch(0, k0 + 64);
+      mma(1);
+    }
+    // D[row 4 lk + v][column lr] of each block
+#pragma unroll
+    for (int v = 0; v < 4; ++v) {
+      tile[32 * wv + lr][4 * lk + v] -= acc0[v];
+      tile[32 * wv + 16 + lr][4 * lk + v] -= acc1[v];
+    }
+    __syncthreads();
+  }
   float w[kCols], rinv[kCols], eta[kCols], code[kCols];
 #pragma unroll
   for (int t = 0; t < kCols; ++t) {
@@ -457,7 +502,10 @@ gptq_status launch_rbt(const float* R, int64_t d, int bi, float* RL,
 gptq_status launch_chain(float* WT, int64_t m, int64_t d, const float* RL,
                          int64_t i0, int bw, int bi, int bits, int64_t gsize,
                          float* scalesP, uint8_t* zerosP, uint8_t* codesP,
-                         float* E, hipStream_t st) {
+                         float* E, const float* R, int64_t sb0, const float* Esb,
+                         hipStream_t st) {
+  const int kn = static_cast<int>(i0 - sb0);
+  if (kn % 32 != 0) return GPTQ_ERR_INVALID_ARG;
   const float maxq = static_cast<float>((1 << bits) - 1);
   int fs = 0;
   if (gsize > 0) {
@@ -468,7 +516,8 @@ gptq_status launch_chain(float* WT, int64_t m, int64_t d, const float* RL,
   const dim3 grid(cdiv(m, kChainRows));
 #define GPTQ_CHAIN(FSV, V)                                                     \
   chain_kernel<FSV, V><<<grid, 256, 0, st>>>(WT, m, d, RL, i0, bw, bi, maxq,  \
-                                             gsize, scalesP, zerosP, codesP, E)
+                                             gsize, scalesP, zerosP, codesP, E, \
+                                             R, sb0, kn, Esb)
 #define GPTQ_CHAIN_FS(V)                     \
   switch (fs) {                              \
     case 0: GPTQ_CHAIN(0, V); break;         \
@@ -503,8 +552,8 @@ gptq_status launch_lazy_update(float* WT, int64_t m, int64_t d, const float* R,
                    reinterpret_cast<uintptr_t>(R) % 16 == 0 &&
                    reinterpret_cast<uintptr_t>(WT) % 16 == 0 &&
                    reinterpret_cast<uintptr_t>(E) % 16 == 0;
-  const int ks = (bw + 3) / 4;      // k steps; bw <= 128
-  const int kpad = ks <= 4 ? 16 : ks <= 8 ? 32 : ks <= 16 ? 64 : 128;
+  const int ks = (bw + 3) / 4;      // k steps; bw <= 4 kLazyMaxKs
+  const int kpad = ks <= 4 ? 16 : ks <= 8 ? 32 : ks <= 16 ? 64 : ks <= 32 ? 128 : ks <= 64 ? 256 : 512;
   if (kpad > bw) {     // rows of E the product reads past bw must be zero
     const int64_t n = int64_t(kpad - bw) * m;
     zero_fill_kernel<<<cdiv(n, 256), 256, 0, st>>>(E + int64_t(bw) * m, n);
@@ -514,7 +563,9 @@ gptq_status launch_lazy_update(float* WT, int64_t m, int64_t d, const float* R,
   if (ks <= 4) GPTQ_LAZY(V, 4);                 \
   else if (ks <= 8) GPTQ_LAZY(V, 8);            \
   else if (ks <= 16) GPTQ_LAZY(V, 16);          \
-  else GPTQ_LAZY(V, 32);
+  else if (ks <= 32) GPTQ_LAZY(V, 32);          \
+  else if (ks <= 64) GPTQ_LAZY(V, 64);          \
+  else GPTQ_LAZY(V, 128);
   if (vec) {
     GPTQ_LAZY_KS(true)
   } else {
