@@ -721,7 +721,9 @@ __global__ __launch_bounds__(256) void trtri_t_kernel(
   const int64_t I0 = 2 * p * s, J0 = I0 + s;
   if (J0 >= d) return;
   const int64_t sJ = min<int64_t>(s, d - J0);
-  const int64_t ti = blockIdx.y, tj = blockIdx.x;
+  // k runs to the end of tile column tj: the heavy columns (large tj) go
+  // first, so the last workgroups dispatched are the short ones
+  const int64_t ti = blockIdx.x, tj = int64_t(gridDim.y) - 1 - blockIdx.y;
   if (ti * 64 >= s || tj * 64 >= sJ) return;
   const int64_t i0 = ti * 64, j0 = tj * 64;
   auto fa = [&](int ii, int64_t k) -> double {
