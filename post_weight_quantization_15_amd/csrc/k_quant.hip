@@ -159,16 +159,19 @@ __device__ inline void row_minmax(float& lo, float& hi) {
 // compensated columns; a group that starts at the block start and reaches
 // past it also reads its later columns from WT (compensated by every
 // earlier block).
+// VEC: 0 = scalar global accesses, 1 = 16-byte ones, 2 = 16-byte ones and
+// a full 128-column block.
 // The quotients w / Delta and rho / R_jj are products with fp32
 // reciprocals; they differ from the IEEE quotients by at most an ulp, which
 // can only matter within 1e-6 of a rounding boundary.
-template <int FS, bool VEC>
+template <int FS, int VEC>
 __global__ __launch_bounds__(256) void chain_kernel(
     const float* __restrict__ WT, int64_t m, int64_t d, const float* __restrict__ RL,
-    int64_t i0, int bw, int bi, float maxq, int64_t gsize,
+    int64_t i0, int bw_arg, int bi, float maxq, int64_t gsize,
     float* __restrict__ scalesP, uint8_t* __restrict__ zerosP,
     uint8_t* __restrict__ codesP, float* __restrict__ E,
     const float* __restrict__ R, int64_t sb0, int kn, const float* __restrict__ Esb) {
+  const int bw = VEC == 2 ? kB : bw_arg;
   __shared__ __attribute__((aligned(16))) float rl[kB * kB];
   __shared__ float tile[kB][kTp];
   __shared__ uint8_t ctile[kB][kChainRows];
@@ -272,12 +275,24 @@ __global__ __launch_bounds__(256) void chain_kernel(
   float scale = scalesP[g0 * m + rs];
   float zero = static_cast<float>(zerosP[g0 * m + rs]);
   float inv_scale = 1.0f / scale;
+  // R rows of the next kPf columns in registers (the LDS latency stays off
+  // the column-to-column dependence)
+  constexpr int kPf = 4;
+  f32x4 pa[kPf], pb[kPf];
+#pragma unroll
+  for (int p = 0; p < kPf; ++p) {
+    const float* rp = rl + (p * kRowLanes + q) * kCols;
+    pa[p] = *reinterpret_cast<const f32x4*>(rp);
+    pb[p] = *reinterpret_cast<const f32x4*>(rp + 4);
+  }
 #pragma clang loop unroll(full)
   for (int tk = 0; tk < kCols; ++tk) {
 #pragma clang loop unroll(full)
   for (int qk = 0; qk < kRowLanes; ++qk) {
     const int k = kRowLanes * tk + qk;
-    if (k >= bw) continue;      // uniform: columns past a partial block
+    // uniform: columns past a partial block (a full block has none, and
+    // its column steps are one straight run the compiler can pipeline)
+    if (VEC != 2 && k >= bw) continue;
     if (FS > 0 && k % (FS > 0 ? FS : 1) == 0 && (i0 + k) % gsize == 0) {
       const int64_t col = i0 + k;
       const int64_t gend = min(col + gsize, d);
@@ -311,13 +326,17 @@ __global__ __launch_bounds__(256) void chain_kernel(
       eta[tk] = e;
     }
     const float eb = row_bcast(e, qk);
-    const float* rk = rl + (k * kRowLanes + q) * kCols;
+    const int sl = k % kPf;
+    const f32x4 ra = pa[sl], rb = pb[sl];
+    if (k + kPf < kB) {
+      const float* rp = rl + ((k + kPf) * kRowLanes + q) * kCols;
+      pa[sl] = *reinterpret_cast<const f32x4*>(rp);
+      pb[sl] = *reinterpret_cast<const f32x4*>(rp + 4);
+    }
     if (tk < 4) {
-      const f32x4 ra = *reinterpret_cast<const f32x4*>(rk);
 #pragma unroll
       for (int t = tk; t < 4; ++t) w[t] = fmaf(-eb, ra[t], w[t]);
     }
-    const f32x4 rb = *reinterpret_cast<const f32x4*>(rk + 4);
 #pragma unroll
     for (int t = (tk > 4 ? tk : 4); t < kCols; ++t) w[t] = fmaf(-eb, rb[t - 4], w[t]);
   }
@@ -530,10 +549,12 @@ gptq_status launch_chain(float* WT, int64_t m, int64_t d, const float* RL,
     case 64: GPTQ_CHAIN(64, V); break;       \
     default: GPTQ_CHAIN(128, V); break;      \
   }
-  if (vec) {
-    GPTQ_CHAIN_FS(true)
+  if (vec && bw == kB) {
+    GPTQ_CHAIN_FS(2)
+  } else if (vec) {
+    GPTQ_CHAIN_FS(1)
   } else {
-    GPTQ_CHAIN_FS(false)
+    GPTQ_CHAIN_FS(0)
   }
 #undef GPTQ_CHAIN_FS
 #undef GPTQ_CHAIN
