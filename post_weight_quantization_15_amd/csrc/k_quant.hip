@@ -328,9 +328,13 @@ __global__ __launch_bounds__(256) void chain_kernel(
     const float eb = row_bcast(e, qk);
     const int sl = k % kPf;
     const f32x4 ra = pa[sl], rb = pb[sl];
+    // keep every element of this column's rows live up to here: a row
+    // register with a dead element could be reused while its load is in
+    // flight, which would make the next load wait
+    asm volatile("" :: "v"(ra), "v"(rb));
     if (k + kPf < kB) {
       const float* rp = rl + ((k + kPf) * kRowLanes + q) * kCols;
-      pa[sl] = *reinterpret_cast<const f32x4*>(rp);
+      if (k + kPf < 4 * kRowLanes) pa[sl] = *reinterpret_cast<const f32x4*>(rp);
       pb[sl] = *reinterpret_cast<const f32x4*>(rp + 4);
     }
     if (tk < 4) {
