@@ -5,12 +5,13 @@
 // The statistic is symmetric, so only the upper triangle is computed and
 // the result is mirrored.
 //
-// bf16 path (the hot path): one workgroup of four wave64s per (256x256 upper
-// super-tile of S, token split); wave w owns the 128x128 sub-tile
-// (w / 2, w % 2) and its 256 fp32 accumulators fill the AGPR file.  The two
-// 256-feature panels of each 32-token step are staged once per workgroup in
-// LDS and shared by the four waves, which halves the L1/L2 traffic per MFMA
-// against waves that load their own operands.
+// bf16 path (the hot path): one workgroup of eight wave64s (two per SIMD,
+// so one wave's LDS waits and barriers overlap the other's MFMAs) per
+// (256x256 upper super-tile of S, token split); wave w owns the 128x64
+// half h = w % 2 of the 128x128 sub-tile (q / 2, q % 2), q = w / 2, and its
+// 128 fp32 accumulators sit in the AGPRs.  The two 256-feature panels of
+// each 32-token step are staged once per workgroup in LDS and shared by the
+// eight waves.
 //  * Unmasked items: global_load_lds_dwordx4 copies the token rows straight
 //    into a four-stage LDS ring (loads run three steps ahead, no VGPRs), and
 //    ds_read_b64_tr_b16 transposes them into v_mfma_f32_16x16x32_bf16
@@ -33,11 +34,11 @@ namespace {
 
 constexpr int kSup = 256;                      // super-tile edge (features)
 constexpr int kStep = 32;                      // tokens per step
-constexpr int kThreads = 256;                  // four wave64s
+constexpr int kThreads = 512;                  // eight wave64s
 constexpr int kPanelBytes = 4 * kSup * 16;     // 4 token chunks x 256 features x 16 B
 constexpr int kStageBytes = 2 * kPanelBytes;
 constexpr int kLdsBytes = 2 * kStageBytes;     // two stages: 64 KiB
-constexpr int kSubElems = 128 * 128;           // one wave's partial tile
+constexpr int kSubElems = 128 * 128;           // one 128x128 sub-tile's partial
 constexpr int kCUs = 256;                      // MI355X compute units
 constexpr int kXcd = 8;                        // accelerator dies, own L2 each
 constexpr int kRegB = 4;                       // XCD regions: blocks of 4x4 super-tiles
@@ -161,9 +162,9 @@ __device__ inline void stage_barrier() {
 }
 
 // acc += A B on v_mfma_f32_16x16x32_bf16 with the accumulator pinned to the
-// AGPR file.  The 256 accumulator registers of a 128x128 sub-tile fill the
-// AGPRs exactly; left to itself the register allocator shuttles them between
-// the two files (and to scratch) once the staging registers are counted.
+// AGPR file: left to itself the register allocator shuttles accumulators
+// between the two files (and to scratch) once the staging registers are
+// counted.
 // Consecutive MFMAs of a step use distinct accumulators; after the last
 // step acc_settle() covers the wait states before the results are read.
 __device__ inline void mfma_acc(f32x4& acc, const u32x4& a, const u32x4& b) {
@@ -174,17 +175,17 @@ __device__ inline void acc_settle() {
   asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" ::: "memory");
 }
 
-// One 32-token step of a wave: 8 + 8 fragment reads, 8 x 8 MFMAs.
+// One 32-token step of a wave: 8 + 4 fragment reads, 8 x 4 MFMAs.
 // acc[a][b] lane l element v = sum over the step's tokens of
-// x[row 16a + 4(l/16) + v] * x[col 16b + l%16] within the wave's sub-tile.
-// The B fragments and the first two A fragments are read up front; A
-// fragment a + 2 is read while the MFMAs of row block a run.
+// x[row 16a + 4(l/16) + v] * x[col 16b + l%16] within the wave's 128x64
+// tile.  The B fragments and the first two A fragments are read up front;
+// A fragment a + 2 is read while the MFMAs of row block a run.
 __device__ inline void mma_step(const char* lds, uint32_t a_off, uint32_t b_off,
-                                const uint32_t offA[8], const uint32_t offB[8],
-                                f32x4 acc[8][8]) {
-  u32x4 fa[8], fb[8];
+                                const uint32_t offA[8], const uint32_t offB[4],
+                                f32x4 acc[8][4]) {
+  u32x4 fa[8], fb[4];
 #pragma unroll
-  for (int b = 0; b < 8; ++b)
+  for (int b = 0; b < 4; ++b)
     fb[b] = *reinterpret_cast<const u32x4*>(lds + b_off + offB[b]);
   fa[0] = *reinterpret_cast<const u32x4*>(lds + a_off + offA[0]);
   fa[1] = *reinterpret_cast<const u32x4*>(lds + a_off + offA[1]);
@@ -192,7 +193,7 @@ __device__ inline void mma_step(const char* lds, uint32_t a_off, uint32_t b_off,
   for (int a = 0; a < 8; ++a) {
     if (a + 2 < 8) fa[a + 2] = *reinterpret_cast<const u32x4*>(lds + a_off + offA[a + 2]);
 #pragma unroll
-    for (int b = 0; b < 8; ++b) {
+    for (int b = 0; b < 4; ++b) {
       mfma_acc(acc[a][b], fa[a], fb[b]);
     }
   }
@@ -202,35 +203,41 @@ __device__ inline void mma_step(const char* lds, uint32_t a_off, uint32_t b_off,
 // split): register-staged loads with zeros outside the data, the step count
 // padded to even with all-zero steps; loads of the steps past the end
 // re-read the last step.
+// The first four waves load and store the stages; all eight compute.
 __device__ inline void run_masked(char* lds, const uint16_t* __restrict__ X,
                                  int64_t ldx, int64_t d, int64_t tbeg,
                                  int64_t tend, int64_t P0, uint32_t b_panel, const uint32_t offA[8],
-                                 const uint32_t offB[8], f32x4 acc[8][8]) {
+                                 const uint32_t offB[4], f32x4 acc[8][4]) {
   const int tid = threadIdx.x;
-  const int lp = tid >> 7, fg = tid & 31, tg = (tid >> 5) & 3;
+  const bool loader = tid < 256;
+  const int lp = (tid >> 7) & 1, fg = tid & 31, tg = (tid >> 5) & 3;
   const uint32_t panel_off = static_cast<uint32_t>(lp) * kPanelBytes;
   const int64_t nst = (tend - tbeg + kStep - 1) / kStep;
   const int64_t nst2 = (nst + 1) & ~int64_t(1);
   auto load_step = [&](int64_t s, u32x4 raw[8]) {
+    if (!loader) return;
     s = s < nst2 ? s : nst2 - 1;
     const int64_t t0 = tbeg + s * kStep;
     load_masked(X, ldx, t0 + 8 * tg, tbeg, tend, P0 + 8 * fg, d, raw);
+  };
+  auto store = [&](uint32_t off, const u32x4 raw[8]) {
+    if (loader) store_panel(lds, off + panel_off, fg, tg, raw);
   };
   // LDS stage k % 2 holds step k; raw0 / raw1 carry the loads of the even /
   // odd step ahead, two steps before their use.
   u32x4 raw0[8], raw1[8];
   load_step(0, raw0);
   load_step(1, raw1);
-  store_panel(lds, panel_off, fg, tg, raw0);
+  store(0, raw0);
   stage_barrier();
   for (int64_t s = 0; s < nst2; s += 2) {
     load_step(s + 2, raw0);
     mma_step(lds, 0, b_panel, offA, offB, acc);
-    store_panel(lds, kStageBytes + panel_off, fg, tg, raw1);
+    store(kStageBytes, raw1);
     stage_barrier();
     load_step(s + 3, raw1);
     mma_step(lds, kStageBytes, kStageBytes + b_panel, offA, offB, acc);
-    store_panel(lds, panel_off, fg, tg, raw0);
+    store(0, raw0);
     stage_barrier();
   }
 }
@@ -282,43 +289,48 @@ __device__ inline void wait_vmcnt_le() {
 
 __device__ inline void run_dma(char* lds, const uint16_t* __restrict__ X,
                                int64_t ldx, int64_t tbeg, int64_t nst,
-                               int64_t F0, int64_t G0, f32x4 acc[8][8]) {
+                               int64_t F0, int64_t G0, f32x4 acc[8][4]) {
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
-  // loader role: wave wv fills panel wv / 2, rows 16 (wv % 2) + 2 i + lane / 32
-  // (instruction i = 0..7); lanes write 16 contiguous bytes each
-  const int p = wv >> 1;
+  // loader role: wave wv fills panel wv / 4, rows 8 (wv % 4) + 2 i + lane / 32
+  // (instruction i = 0..3); lanes write 16 contiguous bytes each
+  const int p = wv >> 2;
   const int64_t P0 = p ? G0 : F0;
-  uint32_t goff[8];
+  uint32_t goff[4];
 #pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    const int r = 16 * (wv & 1) + 2 * i + (lane >> 5);
+  for (int i = 0; i < 4; ++i) {
+    const int r = 8 * (wv & 3) + 2 * i + (lane >> 5);
     const int c = (lane & 31) ^ swz(r);
     goff[i] = static_cast<uint32_t>(2 * (r * ldx + P0 + 8 * c));
   }
-  const uint32_t lds_row0 = static_cast<uint32_t>(p * kDmaPanel + 16 * (wv & 1) * kRowBytes);
-  // MFMA role: sub-tile (wa, wb); lane (kg, j) points at row 8 kg + j / 4,
-  // features 4 (j % 4) .. + 3 of each 16-feature block
-  const int wa = wv >> 1, wb = wv & 1;
+  const uint32_t lds_row0 = static_cast<uint32_t>(p * kDmaPanel + 8 * (wv & 3) * kRowBytes);
+  // MFMA role: half h of sub-tile (wa, wb); lane (kg, j) points at row
+  // 8 kg + j / 4, features 4 (j % 4) .. + 3 of each 16-feature block
+  const int q = wv >> 1, h = wv & 1;
+  const int wa = q >> 1, wb = q & 1;
   const int kg = lane >> 4, j = lane & 15;
   const int r0 = 8 * kg + (j >> 2);
   const int sw = swz(r0);
-  uint32_t aoff[8], boff[8];
+  uint32_t aoff[8], boff[4];
 #pragma unroll
   for (int a = 0; a < 8; ++a) {
     const int cl = 2 * a + ((j & 3) >> 1);
     aoff[a] = static_cast<uint32_t>(r0 * kRowBytes + 16 * ((16 * wa + cl) ^ sw) + 8 * (j & 1));
-    boff[a] = static_cast<uint32_t>(kDmaPanel + r0 * kRowBytes + 16 * ((16 * wb + cl) ^ sw) + 8 * (j & 1));
+  }
+#pragma unroll
+  for (int b = 0; b < 4; ++b) {
+    const int cl = 2 * (4 * h + b) + ((j & 3) >> 1);
+    boff[b] = static_cast<uint32_t>(kDmaPanel + r0 * kRowBytes + 16 * ((16 * wb + cl) ^ sw) + 8 * (j & 1));
   }
 
-  // load i of step k (token rows 2i, 2i + 1 of this wave's half panel)
+  // load i of step k (token rows 2i, 2i + 1 of this wave's quarter panel)
   auto src_of = [&](int64_t k) {
     const int64_t kk = k < nst ? k : nst - 1;
     const uint16_t* base = X + (tbeg + kk * kStep) * ldx;
     asm volatile("" : "+s"(base));
     return reinterpret_cast<const char*>(base);
   };
-  auto dst_of = [&](int64_t k) {
-    return lds + static_cast<uint32_t>(k % kStages) * kDmaStage + lds_row0;
+  auto dst_of = [&](int slot) {
+    return lds + static_cast<uint32_t>(slot) * kDmaStage + lds_row0;
   };
 
 #pragma unroll
@@ -326,35 +338,39 @@ __device__ inline void run_dma(char* lds, const uint16_t* __restrict__ X,
     const char* gb = src_of(k);
     char* dst = dst_of(k);
 #pragma unroll
-    for (int i = 0; i < 8; ++i)
+    for (int i = 0; i < 4; ++i)
       __builtin_amdgcn_global_load_lds((gvoid)(gb + goff[i]), (lvoid)(dst + 2 * i * kRowBytes),
                                        16, 0, 0);
   }
-  wait_vmcnt_le<8 * (kStages - 2)>();
+  wait_vmcnt_le<4 * (kStages - 2)>();
   stage_barrier();
+  // ring slots of step s and of step s + kStages - 1 (the slot before it)
+  int cur = 0, ahead = kStages - 1;
   for (int64_t s = 0; s < nst; ++s) {
-    // the loads of step s + kStages - 1 go out one per row block, between
-    // the MFMAs, so the address unit never holds up the MFMA issue
+    // the loads of step s + kStages - 1 go out one per two row blocks,
+    // between the MFMAs, so the address unit never holds up the MFMA issue
     const char* gb = src_of(s + kStages - 1);
-    char* dst = dst_of(s + kStages - 1);
-    const char* st = lds + static_cast<uint32_t>(s % kStages) * kDmaStage;
-    u32x4 fa[8], fb[8];
+    char* dst = dst_of(ahead);
+    const char* st = lds + static_cast<uint32_t>(cur) * kDmaStage;
+    ahead = cur;
+    cur = (cur + 1 == kStages) ? 0 : cur + 1;
+    u32x4 fa[8], fb[4];
 #pragma unroll
-    for (int b = 0; b < 8; ++b) fb[b] = tr_frag(st, boff[b]);
+    for (int b = 0; b < 4; ++b) fb[b] = tr_frag(st, boff[b]);
     fa[0] = tr_frag(st, aoff[0]);
     fa[1] = tr_frag(st, aoff[1]);
 #pragma unroll
     for (int a = 0; a < 8; ++a) {
 #pragma unroll
-      for (int b = 0; b < 8; ++b) {
+      for (int b = 0; b < 4; ++b) {
         mfma_acc(acc[a][b], fa[a], fb[b]);
-        if (b == 1)
-          __builtin_amdgcn_global_load_lds((gvoid)(gb + goff[a]), (lvoid)(dst + 2 * a * kRowBytes),
-                                           16, 0, 0);
-        if (b == 3 && a + 2 < 8) fa[a + 2] = tr_frag(st, aoff[a + 2]);
+        if (b == 1 && (a & 1) == 0)
+          __builtin_amdgcn_global_load_lds((gvoid)(gb + goff[a >> 1]),
+                                           (lvoid)(dst + 2 * (a >> 1) * kRowBytes), 16, 0, 0);
+        if (b == 2 && a + 2 < 8) fa[a + 2] = tr_frag(st, aoff[a + 2]);
       }
     }
-    wait_vmcnt_le<8 * (kStages - 2)>();
+    wait_vmcnt_le<4 * (kStages - 2)>();
     stage_barrier();
   }
 }
@@ -389,28 +405,28 @@ __global__ __launch_bounds__(kThreads) void hessian_bf16_kernel(
 
   const int tid = threadIdx.x;
   const int lane = tid & 63, wv = tid >> 6;
-  // Loader role: threads 0-127 stage the row panel, 128-255 the column panel
-  // (on a diagonal super-tile both hold the same features).
-  const int64_t P0 = (tid >> 7) ? G0 : F0;
-  // MFMA role: wave wv owns sub-tile (wa, wb).  On a diagonal super-tile the
-  // lower sub-tile (1, 0) mirrors (0, 1): it is computed (keeping the step
-  // free of branches) but not written.
-  const int wa = wv >> 1, wb = wv & 1;
-  const bool busy = !(diag && wv == 2);
+  // Masked loader role: threads 0-127 stage the row panel, 128-255 the
+  // column panel (on a diagonal super-tile both hold the same features).
+  const int64_t P0 = ((tid >> 7) & 1) ? G0 : F0;
+  // MFMA role: wave wv owns half h of sub-tile q = (wa, wb).  On a diagonal
+  // super-tile the lower sub-tile (1, 0) mirrors (0, 1): it is computed
+  // (keeping the step free of branches) but not written.
+  const int q = wv >> 1, h = wv & 1;
+  const int wa = q >> 1, wb = q & 1;
+  const bool busy = !(diag && q == 2);
   const int c = lane >> 4, i16 = lane & 15;
-  uint32_t offA[8], offB[8];
+  uint32_t offA[8], offB[4];
 #pragma unroll
-  for (int a = 0; a < 8; ++a) {
-    offA[a] = lds_unit(c, 128 * wa + 16 * a + i16);
-    offB[a] = lds_unit(c, 128 * wb + 16 * a + i16);
-  }
+  for (int a = 0; a < 8; ++a) offA[a] = lds_unit(c, 128 * wa + 16 * a + i16);
+#pragma unroll
+  for (int b = 0; b < 4; ++b) offB[b] = lds_unit(c, 128 * wb + 64 * h + 16 * b + i16);
   const uint32_t b_panel = static_cast<uint32_t>(kPanelBytes);
 
-  f32x4 acc[8][8];
+  f32x4 acc[8][4];
 #pragma unroll
   for (int a = 0; a < 8; ++a)
 #pragma unroll
-    for (int b = 0; b < 8; ++b) acc[a][b] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int b = 0; b < 4; ++b) acc[a][b] = f32x4{0.f, 0.f, 0.f, 0.f};
 
   if (kFull)
     run_dma(lds, X, ldx, tbeg, ntok / kStep, F0, G0, acc);
@@ -420,7 +436,7 @@ __global__ __launch_bounds__(kThreads) void hessian_bf16_kernel(
   if (!busy) return;
 
   if (nsplit == 1) {
-    // acc[a][b][v] = S(F0 + 128wa + 16a + 4g + v, G0 + 128wb + 16b + i16)
+    // acc[a][b][v] = S(F0 + 128wa + 16a + 4g + v, G0 + 128wb + 64h + 16b + i16)
     const int g = lane >> 4;
 #pragma unroll
     for (int a = 0; a < 8; ++a)
@@ -428,8 +444,8 @@ __global__ __launch_bounds__(kThreads) void hessian_bf16_kernel(
       for (int v = 0; v < 4; ++v) {
         const int64_t i = F0 + 128 * wa + 16 * a + 4 * g + v;
 #pragma unroll
-        for (int b = 0; b < 8; ++b) {
-          const int64_t j = G0 + 128 * wb + 16 * b + i16;
+        for (int b = 0; b < 4; ++b) {
+          const int64_t j = G0 + 128 * wb + 64 * h + 16 * b + i16;
           if (i < d && j < d && i <= j) {
             const float nv = S[i * d + j] + acc[a][b][v];
             S[i * d + j] = nv;
@@ -438,15 +454,17 @@ __global__ __launch_bounds__(kThreads) void hessian_bf16_kernel(
         }
       }
   } else {
-    // native accumulator order: one contiguous 256-byte store per (a, b, v)
-    float* dst = part + ((int64_t(split) * ntiles + upper_index(ti, tj, nt)) * 4 + wv) * kSubElems;
+    // the 128x128 sub-tile's native accumulator order (column blocks
+    // 4h .. 4h + 3 are this wave's): one contiguous 256-byte store per
+    // (a, b, v)
+    float* dst = part + ((int64_t(split) * ntiles + upper_index(ti, tj, nt)) * 4 + q) * kSubElems;
 #pragma unroll
     for (int a = 0; a < 8; ++a)
 #pragma unroll
-      for (int b = 0; b < 8; ++b)
+      for (int b = 0; b < 4; ++b)
 #pragma unroll
         for (int v = 0; v < 4; ++v)
-          dst[((a * 8 + b) * 4 + v) * 64 + lane] = acc[a][b][v];
+          dst[((a * 8 + 4 * h + b) * 4 + v) * 64 + lane] = acc[a][b][v];
   }
 }
 
