@@ -490,14 +490,29 @@ __global__ __launch_bounds__(256) void hessian_reduce_kernel(
   const int64_t ntiles = upper_tiles(nt);
   const float* src = part + (L * 4 + wv) * kSubElems + a * 8 * 4 * 64 + v * 64 + lane;
   const int64_t sstride = ntiles * 4 * kSubElems;
+  // the eight column blocks' sums advance together, four splits per batch
+  // of loads (the additions keep split order)
+  double sum[8] = {0.0, 0.0, 0.0, 0.0, 0.0, 0.0, 0.0, 0.0};
+  for (int s0 = 0; s0 < nsplit; s0 += 4) {
+    float pv[4][8];
+#pragma unroll
+    for (int u = 0; u < 4; ++u)
+#pragma unroll
+      for (int b = 0; b < 8; ++b)
+        pv[u][b] = (s0 + u < nsplit) ? src[(s0 + u) * sstride + b * 4 * 64] : 0.0f;
+#pragma unroll
+    for (int u = 0; u < 4; ++u)
+#pragma unroll
+      for (int b = 0; b < 8; ++b)
+        if (s0 + u < nsplit) sum[b] += pv[u][b];
+  }
+#pragma unroll
   for (int b = 0; b < 8; ++b) {
     const int col = 16 * b + (lane & 15);
     const int64_t j = j0 + col;
-    double sum = 0.0;
-    for (int s = 0; s < nsplit; ++s) sum += src[s * sstride + b * 4 * 64];
     float nv = 0.f;
     if (i < d && j < d && (!diag || i <= j)) {
-      nv = static_cast<float>(static_cast<double>(S[i * d + j]) + sum);
+      nv = static_cast<float>(static_cast<double>(S[i * d + j]) + sum[b]);
       S[i * d + j] = nv;
     }
     band[row][col] = nv;
