@@ -373,6 +373,9 @@ __device__ inline void run_dma(char* lds, const uint16_t* __restrict__ X,
     wait_vmcnt_le<4 * (kStages - 2)>();
     stage_barrier();
   }
+  // the loads issued past the last step (they re-read it) land before the
+  // workgroup's LDS is released
+  wait_vmcnt_le<0>();
 }
 
 // kFull selects the work items this instance runs: the unmasked ones (both
