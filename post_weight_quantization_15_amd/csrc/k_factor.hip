@@ -358,7 +358,8 @@ __device__ inline void diag_store(double* __restrict__ R, int64_t d, int64_t k0,
   if (bad && t == 0) atomicOr(flag, 1);
   for (int e = t; e < kNb * kNb; e += 256) {
     const int r = e >> 6, c = e & 63;
-    if (r < nbk && c < nbk) R[(k0 + r) * d + k0 + c] = (r <= c) ? L.Wl[r][c] : 0.0;
+    // upper part only: every reader of R masks the lower triangle
+    if (r < nbk && c < nbk && r <= c) R[(k0 + r) * d + k0 + c] = L.Wl[r][c];
   }
 }
 
