@@ -41,7 +41,7 @@ constexpr int kLdsBytes = 2 * kStageBytes;     // two stages: 64 KiB
 constexpr int kSubElems = 128 * 128;           // one 128x128 sub-tile's partial
 constexpr int kCUs = 256;                      // MI355X compute units
 constexpr int kXcd = 8;                        // accelerator dies, own L2 each
-constexpr int kRegB = 4;                       // XCD regions: blocks of 4x4 super-tiles
+constexpr int kRegB = 8;                       // work order: blocks of 8x8 super-tiles
 constexpr int64_t kMaxChain = 2048;            // steps per fp32 running sum (see plan_splits)
 constexpr double kMaxPartBytes = 16.0 * (1 << 30);
 
@@ -58,12 +58,14 @@ __device__ inline void tile_of(int64_t L, int nt, int& ti, int& tj) {
   tj = t + static_cast<int>(rem);
 }
 
-// XCD-aware work order.  Workgroup w runs on XCD w % 8, in dispatch order
-// within its XCD.  The upper super-tiles are enumerated block-major (blocks
-// of kRegB x kRegB, row-major over the upper block triangle, row-major inside
-// a block) and cut into 8 consecutive regions, one per XCD; each XCD walks
-// its region split by split.  Concurrent workgroups of one XCD therefore read
-// the same token window of a compact set of panels, which its L2 serves.
+// XCD-aware work order.  The work items (super-tile, token split) form one
+// list, split-major, and within a split the upper super-tiles are enumerated
+// block-major (blocks of kRegB x kRegB, row-major over the upper block
+// triangle, row-major inside a block).  Workgroup w runs on XCD w % 8, in
+// dispatch order within its XCD, and XCD x takes the x-th contiguous eighth
+// of the list.  The workgroups one XCD runs at a time therefore read the same
+// token window of a compact set of panels (a triangle of side 8 or a 4 x 8
+// rectangle of super-tiles touches 8 or 12 of them), which its L2 serves.
 __device__ inline void blocked_tile(int64_t t, int nt, int& ti, int& tj) {
   const int nb = (nt + kRegB - 1) / kRegB;
   for (int br = 0; br < nb; ++br) {
@@ -390,12 +392,13 @@ __global__ __launch_bounds__(kThreads) void hessian_bf16_kernel(
   __shared__ __attribute__((aligned(16))) char lds[kFull ? kStages * kDmaStage : kLdsBytes];
   // work item of this workgroup (see blocked_tile)
   const int64_t ntiles = upper_tiles(nt);
-  const int64_t per_xcd = (ntiles + kXcd - 1) / kXcd;
+  const int64_t nitems = ntiles * nsplit;
+  const int64_t per_xcd = (nitems + kXcd - 1) / kXcd;
   const int64_t w = blockIdx.x;
-  const int64_t pos = w / kXcd;
-  const int split = static_cast<int>(pos / per_xcd);
-  const int64_t t = (w % kXcd) * per_xcd + pos % per_xcd;
-  if (t >= ntiles || split >= nsplit) return;
+  const int64_t item = (w % kXcd) * per_xcd + w / kXcd;
+  if (item >= nitems) return;
+  const int split = static_cast<int>(item / ntiles);
+  const int64_t t = item % ntiles;
   int ti, tj;
   blocked_tile(t, nt, ti, tj);
   const bool diag = ti == tj;
@@ -661,8 +664,8 @@ gptq_status launch_hessian(float* S, int64_t d, const void* X, gptq_dtype dt,
   }
   const int nt = static_cast<int>((d + kSup - 1) / kSup);
   const SplitPlan p = plan_splits(d, n_tok);
-  const int64_t per_xcd = (upper_tiles(nt) + kXcd - 1) / kXcd;
-  const dim3 grid(static_cast<unsigned>(kXcd * per_xcd * p.nsplit));
+  const int64_t per_xcd = (upper_tiles(nt) * p.nsplit + kXcd - 1) / kXcd;
+  const dim3 grid(static_cast<unsigned>(kXcd * per_xcd));
   hessian_bf16_kernel<true><<<grid, kThreads, 0, st>>>(
       static_cast<const uint16_t*>(X), ldx, n_tok, d, nt, p.ks, p.nsplit, S,
       static_cast<float*>(ws));
