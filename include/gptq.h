@@ -15,10 +15,15 @@
  *
  * Conventions shared by every entry point
  *   - Pointers are DEVICE pointers unless marked [host].  The caller owns every
- *     buffer; the library never allocates or frees memory and keeps no state
- *     between calls.  Calls that share a workspace must not overlap.
+ *     buffer; the library never allocates or frees memory.  Its only state
+ *     is one internal stream and two events per device, created on the first
+ *     factor and kept until the process ends.  Calls that share a workspace
+ *     must not overlap.
  *   - `stream` is a hipStream_t passed as void* (NULL = the default stream).
- *     Work is enqueued on it in order.  gptq_cholesky_inverse and
+ *     Work is enqueued on it in order.  The factor also runs part of the
+ *     triangular inverse on the internal stream, forked from `stream` and
+ *     joined back into it by events before the call's later work, so the
+ *     call stays ordered on `stream` as a whole.  gptq_cholesky_inverse and
  *     gptq_quantize_layer (when it factors) enqueue all of a damping
  *     attempt's work, then synchronise `stream` once to read the
  *     positive-definiteness flag; a failed attempt is redone whole.

@@ -58,7 +58,8 @@ gptq_status launch_hessian(float* S, int64_t d, const void* X, gptq_dtype dt,
 struct FactorWs {
   double* H;      // [d, d] damped, permuted Hessian; overwritten by U (upper)
   double* R;      // [d, d] U^-1 (upper)
-  double* T;      // scratch for the triangular inverse
+  double* T;      // scratch for the triangular inverse (caller's stream)
+  double* Tb;     // the same, for the part on the second stream
   double* keys;   // [d] diag(H) after the dead fix
   double* damp;   // [1] damping used
   int* flag;      // [1] set when a pivot is not positive
@@ -73,9 +74,9 @@ gptq_status launch_perm(int64_t d, int act_order, const FactorWs& f,
 gptq_status launch_build_h(const float* S, int64_t d, int64_t n,
                            const int32_t* perm, const uint8_t* dead,
                            const FactorWs& f, hipStream_t st);
-gptq_status launch_cholesky_upper(int64_t d, const FactorWs& f, hipStream_t st);
-gptq_status launch_triangular_inverse(int64_t d, const FactorWs& f,
-                                      hipStream_t st);
+// U (in H) and R = U^-1 (in R), the inverse partly beside the factor on a
+// second stream; the caller's stream has waited for it on return.
+gptq_status launch_factor_inverse(int64_t d, const FactorWs& f, hipStream_t st);
 gptq_status launch_r_to_f32(int64_t d, const FactorWs& f, float* R,
                             hipStream_t st);
 

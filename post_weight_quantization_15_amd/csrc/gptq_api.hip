@@ -97,8 +97,7 @@ gptq_status enqueue_factor(const float* S, int64_t n, int64_t d, float percdamp,
   if ((s = launch_prep_stats(S, d, n, percdamp, attempt, f, dead, st)) != GPTQ_OK) return s;
   if (attempt == 0 && (s = launch_perm(d, act_order, f, perm, st)) != GPTQ_OK) return s;
   if ((s = launch_build_h(S, d, n, perm, dead, f, st)) != GPTQ_OK) return s;
-  if ((s = launch_cholesky_upper(d, f, st)) != GPTQ_OK) return s;
-  if ((s = launch_triangular_inverse(d, f, st)) != GPTQ_OK) return s;
+  if ((s = launch_factor_inverse(d, f, st)) != GPTQ_OK) return s;
   return launch_r_to_f32(d, f, R, st);
 }
 

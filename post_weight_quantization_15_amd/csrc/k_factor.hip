@@ -23,6 +23,8 @@
 // applied level by level (block size 64, 128, 256, ...).
 #include <algorithm>
 #include <cmath>
+#include <functional>
+#include <mutex>
 
 #include "common.h"
 
@@ -717,10 +719,12 @@ __global__ __launch_bounds__(256) void chol_step_kernel(
 
 // Level s: pairs p of adjacent diagonal blocks I = [2ps, 2ps+s),
 // J = [2ps+s, min(2ps+2s, d)).  T_p = U_IJ R_JJ  (R_JJ upper: k <= j).
+// A launch covers pairs p0, p0 + 1, ... (blockIdx.z); pair p's T block
+// starts (p - p0) s^2 into T.
 __global__ __launch_bounds__(256) void trtri_t_kernel(
     const double* __restrict__ U, const double* __restrict__ R,
-    double* __restrict__ T, int64_t d, int64_t s) {
-  const int64_t p = blockIdx.z;
+    double* __restrict__ T, int64_t d, int64_t s, int64_t p0) {
+  const int64_t p = p0 + blockIdx.z;
   const int64_t I0 = 2 * p * s, J0 = I0 + s;
   if (J0 >= d) return;
   const int64_t sJ = min<int64_t>(s, d - J0);
@@ -739,7 +743,7 @@ __global__ __launch_bounds__(256) void trtri_t_kernel(
   f64x4 acc[2][2];
   zero_acc(acc);
   tile_gemm<false>(0, min<int64_t>(sJ, j0 + 64), fa, fb, acc);
-  double* Tp = T + p * s * s;
+  double* Tp = T + (p - p0) * s * s;
   tile_store(acc, [&](int ii, int jj, double v) {
     const int64_t i = i0 + ii, j = j0 + jj;
     if (i < s && j < sJ) Tp[i * s + j] = v;
@@ -749,15 +753,15 @@ __global__ __launch_bounds__(256) void trtri_t_kernel(
 // R_IJ = -R_II T_p  (R_II upper: k >= i).
 __global__ __launch_bounds__(256) void trtri_r_kernel(
     double* __restrict__ R, const double* __restrict__ T, int64_t d,
-    int64_t s) {
-  const int64_t p = blockIdx.z;
+    int64_t s, int64_t p0) {
+  const int64_t p = p0 + blockIdx.z;
   const int64_t I0 = 2 * p * s, J0 = I0 + s;
   if (J0 >= d) return;
   const int64_t sJ = min<int64_t>(s, d - J0);
   const int64_t ti = blockIdx.y, tj = blockIdx.x;
   if (ti * 64 >= s || tj * 64 >= sJ) return;
   const int64_t i0 = ti * 64, j0 = tj * 64;
-  const double* Tp = T + p * s * s;
+  const double* Tp = T + (p - p0) * s * s;
   auto fa = [&](int ii, int64_t k) -> double {
     const int64_t i = i0 + ii;
     return (k >= i) ? R[(I0 + i) * d + I0 + k] : 0.0;
@@ -804,6 +808,7 @@ FactorWs carve_factor_ws(Carver& c, int64_t d) {
     tmax = std::max(tmax, pairs * s * s);
   }
   f.T = c.take<double>(size_t(std::max<int64_t>(tmax, 1)));
+  f.Tb = c.take<double>(size_t(std::max<int64_t>(tmax, 1)));
   f.keys = c.take<double>(size_t(d));
   f.damp = c.take<double>(1);
   f.flag = c.take<int>(1);
@@ -838,8 +843,12 @@ gptq_status launch_build_h(const float* S, int64_t d, int64_t n,
   return GPTQ_OK;
 }
 
-gptq_status launch_cholesky_upper(int64_t d, const FactorWs& f,
-                                  hipStream_t st) {
+// at_split, when given, is called right after the launch of the step kernel
+// of the block starting at column split_k: from there on the columns
+// [split_k, d) of U (and R's diagonal blocks in them) are final.
+gptq_status launch_cholesky_upper(int64_t d, const FactorWs& f, hipStream_t st,
+                                  int64_t split_k,
+                                  const std::function<gptq_status()>& at_split) {
   zero_flag_kernel<<<1, 1, 0, st>>>(f.flag);
   GPTQ_CHECK_LAUNCH();
   // 64-column blocks, 64-aligned from the top (the bottom one absorbs
@@ -892,6 +901,10 @@ gptq_status launch_cholesky_upper(int64_t d, const FactorWs& f,
           f.H, f.R, d, bk0[x], bnb[x], x > 0 ? bk0[x - 1] : -1, x > 0 ? bnb[x - 1] : 0,
           kg, f.flag, bk, bK, ta, tb - ta);
       GPTQ_CHECK_LAUNCH();
+      if (bk0[x] == split_k && at_split) {
+        const gptq_status rc = at_split();
+        if (rc != GPTQ_OK) return rc;
+      }
     }
     // deferred work must have found a launch: it exists only when the next
     // group has all of its blocks below row 0
@@ -921,20 +934,115 @@ gptq_status launch_cholesky_upper(int64_t d, const FactorWs& f,
   return GPTQ_OK;
 }
 
-gptq_status launch_triangular_inverse(int64_t d, const FactorWs& f,
-                                      hipStream_t st) {
-  // The diagonal blocks of R (64-aligned from the top, the last one partial)
-  // were formed by the Cholesky's diagonal kernel; combine them level by
-  // level.
-  for (int64_t s = kNb; s < d; s *= 2) {
-    const unsigned pairs = cdiv(d, 2 * s);
-    const dim3 grid(cdiv(s, 64), cdiv(s, 64), pairs);
-    trtri_t_kernel<<<grid, 256, 0, st>>>(f.H, f.R, f.T, d, s);
-    GPTQ_CHECK_LAUNCH();
-    trtri_r_kernel<<<grid, 256, 0, st>>>(f.R, f.T, d, s);
-    GPTQ_CHECK_LAUNCH();
-  }
+namespace {
+
+// One product of level s for pairs p0 .. p0 + np - 1 (T blocks in T).
+gptq_status launch_trtri_t(int64_t d, const FactorWs& f, double* T, int64_t s,
+                           int64_t p0, int64_t np, hipStream_t st) {
+  if (np <= 0) return GPTQ_OK;
+  const dim3 grid(cdiv(s, 64), cdiv(s, 64), static_cast<unsigned>(np));
+  trtri_t_kernel<<<grid, 256, 0, st>>>(f.H, f.R, T, d, s, p0);
+  GPTQ_CHECK_LAUNCH();
   return GPTQ_OK;
+}
+
+gptq_status launch_trtri_r(int64_t d, const FactorWs& f, const double* T, int64_t s,
+                           int64_t p0, int64_t np, hipStream_t st) {
+  if (np <= 0) return GPTQ_OK;
+  const dim3 grid(cdiv(s, 64), cdiv(s, 64), static_cast<unsigned>(np));
+  trtri_r_kernel<<<grid, 256, 0, st>>>(f.R, T, d, s, p0);
+  GPTQ_CHECK_LAUNCH();
+  return GPTQ_OK;
+}
+
+// A second stream per device (default priority, created on first use) and
+// the two events that order it against the caller's stream.
+struct SideStream {
+  hipStream_t st = nullptr;
+  hipEvent_t ready = nullptr, done = nullptr;
+};
+constexpr int kMaxDevices = 64;
+std::mutex g_side_mu;
+SideStream g_side[kMaxDevices];
+
+gptq_status side_stream(SideStream** out) {
+  *out = nullptr;
+  int dev = 0;
+  GPTQ_CHECK_HIP(hipGetDevice(&dev));
+  if (dev < 0 || dev >= kMaxDevices) return GPTQ_OK;
+  SideStream& sd = g_side[dev];
+  if (!sd.st) {
+    hipStream_t st = nullptr;
+    GPTQ_CHECK_HIP(hipStreamCreateWithFlags(&st, hipStreamNonBlocking));
+    GPTQ_CHECK_HIP(hipEventCreateWithFlags(&sd.ready, hipEventDisableTiming));
+    GPTQ_CHECK_HIP(hipEventCreateWithFlags(&sd.done, hipEventDisableTiming));
+    sd.st = st;
+  }
+  *out = &sd;
+  return GPTQ_OK;
+}
+
+}  // namespace
+
+// The reverse Cholesky H = U U^T followed by R = U^-1.  The inverse combines
+// R's 64x64 diagonal blocks level by level; its top level pairs I = [0, s)
+// with J = [s, d) (s the largest level).  The factor runs from the bottom
+// up, so U's columns J are final once it has passed column s: from there
+// the levels below the top inside J and the top level's T = U_IJ R_JJ run on
+// a second stream, beside the factor of the columns I, which is latency
+// bound and leaves most of the chip idle.  The rest (the levels inside I,
+// then R_IJ = -R_II T) follows the factor on the caller's stream, after it
+// has waited for the second stream.  The two streams touch disjoint parts of
+// H, R and the scratch (T for the caller's stream, Tb for the other).
+// Calls from several host threads are serialised while they enqueue.
+gptq_status launch_factor_inverse(int64_t d, const FactorWs& f, hipStream_t st) {
+  int64_t s_top = 0;
+  for (int64_t s = kNb; s < d; s *= 2) s_top = s;
+  std::lock_guard<std::mutex> lock(g_side_mu);
+  SideStream* side = nullptr;
+  if (s_top > 0) {
+    const gptq_status rc = side_stream(&side);
+    if (rc != GPTQ_OK) return rc;
+  }
+  if (!side) {
+    // one stream: the factor, then every level in order
+    const gptq_status rc = launch_cholesky_upper(d, f, st, -1, nullptr);
+    if (rc != GPTQ_OK) return rc;
+    for (int64_t s = kNb; s < d; s *= 2) {
+      const int64_t np = cdiv(d, 2 * s);
+      gptq_status r2;
+      if ((r2 = launch_trtri_t(d, f, f.T, s, 0, np, st)) != GPTQ_OK) return r2;
+      if ((r2 = launch_trtri_r(d, f, f.T, s, 0, np, st)) != GPTQ_OK) return r2;
+    }
+    return GPTQ_OK;
+  }
+  bool forked = false;
+  auto at_split = [&]() -> gptq_status {
+    GPTQ_CHECK_HIP(hipEventRecord(side->ready, st));
+    GPTQ_CHECK_HIP(hipStreamWaitEvent(side->st, side->ready, 0));
+    forked = true;
+    gptq_status rc = GPTQ_OK;
+    for (int64_t s = kNb; s < s_top && rc == GPTQ_OK; s *= 2) {
+      const int64_t p0 = s_top / (2 * s);
+      const int64_t np = int64_t(cdiv(d, 2 * s)) - p0;
+      rc = launch_trtri_t(d, f, f.Tb, s, p0, np, side->st);
+      if (rc == GPTQ_OK) rc = launch_trtri_r(d, f, f.Tb, s, p0, np, side->st);
+    }
+    if (rc == GPTQ_OK) rc = launch_trtri_t(d, f, f.Tb, s_top, 0, 1, side->st);
+    // recorded even after a failed launch, so the caller's stream can join
+    GPTQ_CHECK_HIP(hipEventRecord(side->done, side->st));
+    return rc;
+  };
+  gptq_status rc = launch_cholesky_upper(d, f, st, s_top, at_split);
+  for (int64_t s = kNb; s < s_top && rc == GPTQ_OK; s *= 2) {
+    const int64_t np = s_top / (2 * s);
+    rc = launch_trtri_t(d, f, f.T, s, 0, np, st);
+    if (rc == GPTQ_OK) rc = launch_trtri_r(d, f, f.T, s, 0, np, st);
+  }
+  if (forked) GPTQ_CHECK_HIP(hipStreamWaitEvent(st, side->done, 0));
+  if (rc != GPTQ_OK) return rc;
+  if (!forked) return GPTQ_ERR_HIP;  // the factor never reached column s_top
+  return launch_trtri_r(d, f, f.Tb, s_top, 0, 1, st);
 }
 
 gptq_status launch_r_to_f32(int64_t d, const FactorWs& f, float* R,
