@@ -719,64 +719,76 @@ __global__ __launch_bounds__(256) void chol_step_kernel(
 
 // Level s: pairs p of adjacent diagonal blocks I = [2ps, 2ps+s),
 // J = [2ps+s, min(2ps+2s, d)).  T_p = U_IJ R_JJ  (R_JJ upper: k <= j).
-// A launch covers pairs p0, p0 + 1, ... (blockIdx.z); pair p's T block
-// starts (p - p0) s^2 into T.
+// A launch covers the 64x64 tiles of pairs p0 .. p0 + np - 1, item w =
+// (tile column, tile row, pair) with the first fastest, each workgroup
+// taking items blockIdx.x, blockIdx.x + gridDim.x, ... (a grid smaller than
+// the item count leaves the rest of the chip to other work); pair p's T
+// block starts (p - p0) s^2 into T.
 __global__ __launch_bounds__(256) void trtri_t_kernel(
     const double* __restrict__ U, const double* __restrict__ R,
-    double* __restrict__ T, int64_t d, int64_t s, int64_t p0) {
-  const int64_t p = p0 + blockIdx.z;
-  const int64_t I0 = 2 * p * s, J0 = I0 + s;
-  if (J0 >= d) return;
-  const int64_t sJ = min<int64_t>(s, d - J0);
-  // k runs to the end of tile column tj: the heavy columns (large tj) go
-  // first, so the last workgroups dispatched are the short ones
-  const int64_t ti = blockIdx.x, tj = int64_t(gridDim.y) - 1 - blockIdx.y;
-  if (ti * 64 >= s || tj * 64 >= sJ) return;
-  const int64_t i0 = ti * 64, j0 = tj * 64;
-  auto fa = [&](int ii, int64_t k) -> double {
-    return (k < sJ) ? U[(I0 + i0 + ii) * d + J0 + k] : 0.0;
-  };
-  auto fb = [&](int64_t k, int jj) -> double {
-    const int64_t j = j0 + jj;
-    return (k <= j && j < sJ) ? R[(J0 + k) * d + J0 + j] : 0.0;
-  };
-  f64x4 acc[2][2];
-  zero_acc(acc);
-  tile_gemm<false>(0, min<int64_t>(sJ, j0 + 64), fa, fb, acc);
-  double* Tp = T + (p - p0) * s * s;
-  tile_store(acc, [&](int ii, int jj, double v) {
-    const int64_t i = i0 + ii, j = j0 + jj;
-    if (i < s && j < sJ) Tp[i * s + j] = v;
-  });
+    double* __restrict__ T, int64_t d, int64_t s, int64_t p0, int64_t np) {
+  const int64_t g = (s + 63) / 64, nitems = g * g * np;
+  for (int64_t w = blockIdx.x; w < nitems; w += gridDim.x) {
+    __syncthreads();                           // the previous item's LDS reads
+    const int64_t p = p0 + w / (g * g);
+    const int64_t I0 = 2 * p * s, J0 = I0 + s;
+    if (J0 >= d) continue;
+    const int64_t sJ = min<int64_t>(s, d - J0);
+    // k runs to the end of tile column tj: the heavy columns (large tj) come
+    // first, so the last items are the short ones
+    const int64_t ti = w % g, tj = g - 1 - (w / g) % g;
+    if (ti * 64 >= s || tj * 64 >= sJ) continue;
+    const int64_t i0 = ti * 64, j0 = tj * 64;
+    auto fa = [&](int ii, int64_t k) -> double {
+      return (k < sJ) ? U[(I0 + i0 + ii) * d + J0 + k] : 0.0;
+    };
+    auto fb = [&](int64_t k, int jj) -> double {
+      const int64_t j = j0 + jj;
+      return (k <= j && j < sJ) ? R[(J0 + k) * d + J0 + j] : 0.0;
+    };
+    f64x4 acc[2][2];
+    zero_acc(acc);
+    tile_gemm<false>(0, min<int64_t>(sJ, j0 + 64), fa, fb, acc);
+    double* Tp = T + (p - p0) * s * s;
+    tile_store(acc, [&](int ii, int jj, double v) {
+      const int64_t i = i0 + ii, j = j0 + jj;
+      if (i < s && j < sJ) Tp[i * s + j] = v;
+    });
+  }
 }
 
-// R_IJ = -R_II T_p  (R_II upper: k >= i).
+// R_IJ = -R_II T_p  (R_II upper: k >= i); items as above, tile rows with the
+// longest k range (small ti) first.
 __global__ __launch_bounds__(256) void trtri_r_kernel(
     double* __restrict__ R, const double* __restrict__ T, int64_t d,
-    int64_t s, int64_t p0) {
-  const int64_t p = p0 + blockIdx.z;
-  const int64_t I0 = 2 * p * s, J0 = I0 + s;
-  if (J0 >= d) return;
-  const int64_t sJ = min<int64_t>(s, d - J0);
-  const int64_t ti = blockIdx.y, tj = blockIdx.x;
-  if (ti * 64 >= s || tj * 64 >= sJ) return;
-  const int64_t i0 = ti * 64, j0 = tj * 64;
-  const double* Tp = T + (p - p0) * s * s;
-  auto fa = [&](int ii, int64_t k) -> double {
-    const int64_t i = i0 + ii;
-    return (k >= i) ? R[(I0 + i) * d + I0 + k] : 0.0;
-  };
-  auto fb = [&](int64_t k, int jj) -> double {
-    const int64_t j = j0 + jj;
-    return (j < sJ) ? Tp[k * s + j] : 0.0;
-  };
-  f64x4 acc[2][2];
-  zero_acc(acc);
-  tile_gemm<false>(i0, s, fa, fb, acc);
-  tile_store(acc, [&](int ii, int jj, double v) {
-    const int64_t i = i0 + ii, j = j0 + jj;
-    if (i < s && j < sJ) R[(I0 + i) * d + J0 + j] = -v;
-  });
+    int64_t s, int64_t p0, int64_t np) {
+  const int64_t g = (s + 63) / 64, nitems = g * g * np;
+  for (int64_t w = blockIdx.x; w < nitems; w += gridDim.x) {
+    __syncthreads();
+    const int64_t p = p0 + w / (g * g);
+    const int64_t I0 = 2 * p * s, J0 = I0 + s;
+    if (J0 >= d) continue;
+    const int64_t sJ = min<int64_t>(s, d - J0);
+    const int64_t ti = (w / g) % g, tj = w % g;
+    if (ti * 64 >= s || tj * 64 >= sJ) continue;
+    const int64_t i0 = ti * 64, j0 = tj * 64;
+    const double* Tp = T + (p - p0) * s * s;
+    auto fa = [&](int ii, int64_t k) -> double {
+      const int64_t i = i0 + ii;
+      return (k >= i) ? R[(I0 + i) * d + I0 + k] : 0.0;
+    };
+    auto fb = [&](int64_t k, int jj) -> double {
+      const int64_t j = j0 + jj;
+      return (j < sJ) ? Tp[k * s + j] : 0.0;
+    };
+    f64x4 acc[2][2];
+    zero_acc(acc);
+    tile_gemm<false>(i0, s, fa, fb, acc);
+    tile_store(acc, [&](int ii, int jj, double v) {
+      const int64_t i = i0 + ii, j = j0 + jj;
+      if (i < s && j < sJ) R[(I0 + i) * d + J0 + j] = -v;
+    });
+  }
 }
 
 __global__ __launch_bounds__(256) void r_to_f32_kernel(
@@ -936,24 +948,32 @@ gptq_status launch_cholesky_upper(int64_t d, const FactorWs& f, hipStream_t st,
 
 namespace {
 
-// One product of level s for pairs p0 .. p0 + np - 1 (T blocks in T).
+// One product of level s for pairs p0 .. p0 + np - 1 (T blocks in T), on
+// at most max_wg workgroups.
 gptq_status launch_trtri_t(int64_t d, const FactorWs& f, double* T, int64_t s,
-                           int64_t p0, int64_t np, hipStream_t st) {
+                           int64_t p0, int64_t np, int64_t max_wg, hipStream_t st) {
   if (np <= 0) return GPTQ_OK;
-  const dim3 grid(cdiv(s, 64), cdiv(s, 64), static_cast<unsigned>(np));
-  trtri_t_kernel<<<grid, 256, 0, st>>>(f.H, f.R, T, d, s, p0);
+  const int64_t g = (s + 63) / 64;
+  const unsigned grid = static_cast<unsigned>(std::min<int64_t>(g * g * np, max_wg));
+  trtri_t_kernel<<<grid, 256, 0, st>>>(f.H, f.R, T, d, s, p0, np);
   GPTQ_CHECK_LAUNCH();
   return GPTQ_OK;
 }
 
 gptq_status launch_trtri_r(int64_t d, const FactorWs& f, const double* T, int64_t s,
-                           int64_t p0, int64_t np, hipStream_t st) {
+                           int64_t p0, int64_t np, int64_t max_wg, hipStream_t st) {
   if (np <= 0) return GPTQ_OK;
-  const dim3 grid(cdiv(s, 64), cdiv(s, 64), static_cast<unsigned>(np));
-  trtri_r_kernel<<<grid, 256, 0, st>>>(f.R, T, d, s, p0);
+  const int64_t g = (s + 63) / 64;
+  const unsigned grid = static_cast<unsigned>(std::min<int64_t>(g * g * np, max_wg));
+  trtri_r_kernel<<<grid, 256, 0, st>>>(f.R, T, d, s, p0, np);
   GPTQ_CHECK_LAUNCH();
   return GPTQ_OK;
 }
+
+// Workgroups of the inverse's launches beside the factor: the step kernels
+// keep the rest of the chip.
+constexpr int64_t kSideWg = 96;
+constexpr int64_t kAllWg = int64_t(1) << 30;
 
 // A second stream per device (default priority, created on first use) and
 // the two events that order it against the caller's stream.
@@ -1011,8 +1031,8 @@ gptq_status launch_factor_inverse(int64_t d, const FactorWs& f, hipStream_t st) 
     for (int64_t s = kNb; s < d; s *= 2) {
       const int64_t np = cdiv(d, 2 * s);
       gptq_status r2;
-      if ((r2 = launch_trtri_t(d, f, f.T, s, 0, np, st)) != GPTQ_OK) return r2;
-      if ((r2 = launch_trtri_r(d, f, f.T, s, 0, np, st)) != GPTQ_OK) return r2;
+      if ((r2 = launch_trtri_t(d, f, f.T, s, 0, np, kAllWg, st)) != GPTQ_OK) return r2;
+      if ((r2 = launch_trtri_r(d, f, f.T, s, 0, np, kAllWg, st)) != GPTQ_OK) return r2;
     }
     return GPTQ_OK;
   }
@@ -1025,10 +1045,10 @@ gptq_status launch_factor_inverse(int64_t d, const FactorWs& f, hipStream_t st) 
     for (int64_t s = kNb; s < s_top && rc == GPTQ_OK; s *= 2) {
       const int64_t p0 = s_top / (2 * s);
       const int64_t np = int64_t(cdiv(d, 2 * s)) - p0;
-      rc = launch_trtri_t(d, f, f.Tb, s, p0, np, side->st);
-      if (rc == GPTQ_OK) rc = launch_trtri_r(d, f, f.Tb, s, p0, np, side->st);
+      rc = launch_trtri_t(d, f, f.Tb, s, p0, np, kSideWg, side->st);
+      if (rc == GPTQ_OK) rc = launch_trtri_r(d, f, f.Tb, s, p0, np, kSideWg, side->st);
     }
-    if (rc == GPTQ_OK) rc = launch_trtri_t(d, f, f.Tb, s_top, 0, 1, side->st);
+    if (rc == GPTQ_OK) rc = launch_trtri_t(d, f, f.Tb, s_top, 0, 1, kSideWg, side->st);
     // recorded even after a failed launch, so the caller's stream can join
     GPTQ_CHECK_HIP(hipEventRecord(side->done, side->st));
     return rc;
@@ -1036,13 +1056,13 @@ gptq_status launch_factor_inverse(int64_t d, const FactorWs& f, hipStream_t st) 
   gptq_status rc = launch_cholesky_upper(d, f, st, s_top, at_split);
   for (int64_t s = kNb; s < s_top && rc == GPTQ_OK; s *= 2) {
     const int64_t np = s_top / (2 * s);
-    rc = launch_trtri_t(d, f, f.T, s, 0, np, st);
-    if (rc == GPTQ_OK) rc = launch_trtri_r(d, f, f.T, s, 0, np, st);
+    rc = launch_trtri_t(d, f, f.T, s, 0, np, kAllWg, st);
+    if (rc == GPTQ_OK) rc = launch_trtri_r(d, f, f.T, s, 0, np, kAllWg, st);
   }
   if (forked) GPTQ_CHECK_HIP(hipStreamWaitEvent(st, side->done, 0));
   if (rc != GPTQ_OK) return rc;
   if (!forked) return GPTQ_ERR_HIP;  // the factor never reached column s_top
-  return launch_trtri_r(d, f, f.Tb, s_top, 0, 1, st);
+  return launch_trtri_r(d, f, f.Tb, s_top, 0, 1, kAllWg, st);
 }
 
 gptq_status launch_r_to_f32(int64_t d, const FactorWs& f, float* R,
