@@ -346,11 +346,21 @@ __device__ inline void run_dma(char* lds, const uint16_t* __restrict__ X,
   }
   wait_vmcnt_le<4 * (kStages - 2)>();
   stage_barrier();
+  // Each step is two halves (row blocks 0-3, 4-7) ending in a barrier.  The
+  // second wave of each SIMD (waves 4-7) runs one half behind the first:
+  // after every barrier one of a SIMD's two waves starts a step (fragment
+  // reads first) while the other is in its second half, whose first
+  // fragments it read before the barrier, and keeps the MFMA pipe busy.
+  // Ordering of the ring under this skew: the loads of step s + 3 go out in
+  // the second half of step s, when both waves are done with step s - 1
+  // (the slot they refill); each wave waits for its loads of step s + 1 at
+  // the end of the first half of step s, before the barrier after which the
+  // leading waves start reading it.
+  const bool late = wv >= 4;
+  if (late) stage_barrier();
   // ring slots of step s and of step s + kStages - 1 (the slot before it)
   int cur = 0, ahead = kStages - 1;
   for (int64_t s = 0; s < nst; ++s) {
-    // the loads of step s + kStages - 1 go out one per two row blocks,
-    // between the MFMAs, so the address unit never holds up the MFMA issue
     const char* gb = src_of(s + kStages - 1);
     char* dst = dst_of(ahead);
     const char* st = lds + static_cast<uint32_t>(cur) * kDmaStage;
@@ -366,15 +376,20 @@ __device__ inline void run_dma(char* lds, const uint16_t* __restrict__ X,
 #pragma unroll
       for (int b = 0; b < 4; ++b) {
         mfma_acc(acc[a][b], fa[a], fb[b]);
-        if (b == 1 && (a & 1) == 0)
-          __builtin_amdgcn_global_load_lds((gvoid)(gb + goff[a >> 1]),
-                                           (lvoid)(dst + 2 * (a >> 1) * kRowBytes), 16, 0, 0);
+        if (b == 1 && a >= 4)
+          __builtin_amdgcn_global_load_lds((gvoid)(gb + goff[a - 4]),
+                                           (lvoid)(dst + 2 * (a - 4) * kRowBytes), 16, 0, 0);
         if (b == 2 && a + 2 < 8) fa[a + 2] = tr_frag(st, aoff[a + 2]);
       }
+      if (a == 3) {
+        wait_vmcnt_le<4 * (kStages - 3)>();
+        stage_barrier();
+      }
     }
-    wait_vmcnt_le<4 * (kStages - 2)>();
     stage_barrier();
   }
+  // as many barriers for every wave; after this one no wave reads the ring
+  if (!late) stage_barrier();
   // the loads issued past the last step (they re-read it) land before the
   // workgroup's LDS is released
   wait_vmcnt_le<0>();
