@@ -318,11 +318,14 @@ __global__ __launch_bounds__(256) void chain_kernel(
         zerosP[(col / gsize) * m + r] = static_cast<uint8_t>(zero);
       }
     }
+    // c - z = clamp(rint(x / scale), -z, maxq - z) (small integers, exact),
+    // and w - q = x - scale (c - z) in one rounding: six dependent
+    // operations from the column's value to its residual
     const float x = w[tk];
-    const float c = fminf(fmaxf(rintf(x * inv_scale) + zero, 0.0f), maxq);
-    const float e = (x - scale * (c - zero)) * rinv[tk];
+    const float cz = fminf(fmaxf(rintf(x * inv_scale), -zero), maxq - zero);
+    const float e = fmaf(-scale, cz, x) * rinv[tk];
     if (q == qk) {
-      code[tk] = c;
+      code[tk] = cz + zero;
       eta[tk] = e;
     }
     const float eb = row_bcast(e, qk);
