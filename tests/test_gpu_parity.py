@@ -153,6 +153,34 @@ def test_factor_not_spd(dev):
     assert ei.value.status == gq.GPTQ_ERR_NOT_SPD
 
 
+def test_factor_and_layer_on_user_stream(dev):
+    """Part of the triangular inverse runs on the library's own stream, forked
+    from the caller's stream and joined back into it.  On a caller stream
+    other than the default one the factor (whose arithmetic has a fixed
+    order) gives the same bits as on the default stream, and so does a
+    layer quantized there with the factor inside the call."""
+    d, n = 1100, 4410
+    X = synth.decaying_spectrum_acts(d, n, 12, "fac/stream", "cpu", dtype=torch.float32)
+    S = torch.from_numpy(orc.hessian_sum(np64(X)).astype(np.float32)).to(dev)
+    W = synth.normal_weight(96, d, 0.02, 12, "fac/stream/W", "cpu").to(dev)
+    params = dict(bits=4, group_size=-1, blocksize=128, percdamp=0.01, act_order=True)
+    R0, perm0, dead0, _ = gq.gptq_cholesky_inverse(S, n, 0.01, True)
+    out0 = gq.gptq_quantize_layer(W, S, n, **params)          # factors inside
+    torch.cuda.synchronize()
+    side = torch.cuda.Stream(device=dev)
+    side.wait_stream(torch.cuda.current_stream(dev))
+    with torch.cuda.stream(side):
+        R1, perm1, dead1, _ = gq.gptq_cholesky_inverse(S, n, 0.01, True)
+        out1 = gq.gptq_quantize_layer(W, S, n, **params)
+        host = {k: v.to("cpu", non_blocking=False) for k, v in out1.items()}
+        R1h = R1.cpu()
+    side.synchronize()
+    assert torch.equal(R1h, R0.cpu())
+    assert torch.equal(perm1.cpu(), perm0.cpu()) and torch.equal(dead1.cpu(), dead0.cpu())
+    for k, v in out0.items():
+        assert torch.equal(host[k], v.cpu()), k
+
+
 # ----------------------------------------------------------------------------
 # Whole layer
 # ----------------------------------------------------------------------------
