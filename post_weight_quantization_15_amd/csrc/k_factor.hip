@@ -985,17 +985,30 @@ constexpr int kMaxDevices = 64;
 std::mutex g_side_mu;
 SideStream g_side[kMaxDevices];
 
-gptq_status side_stream(SideStream** out) {
+// The second stream of the device that runs `caller` (the current device for
+// the null stream), created with that device current.
+gptq_status side_stream(hipStream_t caller, SideStream** out) {
   *out = nullptr;
   int dev = 0;
-  GPTQ_CHECK_HIP(hipGetDevice(&dev));
+  if (caller)
+    GPTQ_CHECK_HIP(hipStreamGetDevice(caller, &dev));
+  else
+    GPTQ_CHECK_HIP(hipGetDevice(&dev));
   if (dev < 0 || dev >= kMaxDevices) return GPTQ_OK;
   SideStream& sd = g_side[dev];
   if (!sd.st) {
+    int cur = 0;
+    GPTQ_CHECK_HIP(hipGetDevice(&cur));
+    if (cur != dev) GPTQ_CHECK_HIP(hipSetDevice(dev));
     hipStream_t st = nullptr;
-    GPTQ_CHECK_HIP(hipStreamCreateWithFlags(&st, hipStreamNonBlocking));
-    GPTQ_CHECK_HIP(hipEventCreateWithFlags(&sd.ready, hipEventDisableTiming));
-    GPTQ_CHECK_HIP(hipEventCreateWithFlags(&sd.done, hipEventDisableTiming));
+    hipEvent_t ready = nullptr, done = nullptr;
+    const bool ok = hipStreamCreateWithFlags(&st, hipStreamNonBlocking) == hipSuccess &&
+                    hipEventCreateWithFlags(&ready, hipEventDisableTiming) == hipSuccess &&
+                    hipEventCreateWithFlags(&done, hipEventDisableTiming) == hipSuccess;
+    if (cur != dev) GPTQ_CHECK_HIP(hipSetDevice(cur));
+    if (!ok) return GPTQ_ERR_HIP;
+    sd.ready = ready;
+    sd.done = done;
     sd.st = st;
   }
   *out = &sd;
@@ -1021,7 +1034,7 @@ gptq_status launch_factor_inverse(int64_t d, const FactorWs& f, hipStream_t st) 
   std::lock_guard<std::mutex> lock(g_side_mu);
   SideStream* side = nullptr;
   if (s_top > 0) {
-    const gptq_status rc = side_stream(&side);
+    const gptq_status rc = side_stream(st, &side);
     if (rc != GPTQ_OK) return rc;
   }
   if (!side) {
