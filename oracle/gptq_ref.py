@@ -24,6 +24,15 @@ reading independently; "parity unpinned" = no page fixes a value for it):
   * group_size > 0: dynamic groups -- refitted at each group start, in
     processing order, on the current working weights ([derivation] 8.3/8.4);
     group_id[perm[j]] = j // g.                                 parity unpinned
+  * Symmetric grid ([derivation] 1.1 names symmetric grids, 8.4 the signed
+    code form): range [-a, a], a = max|w| (0 in range), 2^b - 1 levels
+    -h..h with h = 2^(b-1) - 1, Delta = a / h; codes stored signed (c - h)
+    in b-bit two's complement.  At b = 2 this is the ternary grid
+    {-1, 0, +1} Delta of [teardown] "extreme quantization".  parity unpinned
+  * Static groups ([derivation] 8.3): each group's grid is fitted before
+    GPTQ on the ORIGINAL contiguous columns of the original row (dead
+    columns included, like the whole-row grid); processing position j uses
+    group floor(perm[j] / g); group_id is then the trivial k // g.
   * A group start must see fully compensated columns: every group that starts
     inside a block must end inside it.  Other (g, blocksize) pairs are
     rejected.                                                  parity unpinned
@@ -49,7 +58,8 @@ __all__ = [
     "factor", "check_group_layout", "quantize_columns", "gptq_layer",
     "pack_codes", "unpack_codes", "layer_error", "proxy_loss",
     "obs_criterion", "obs_update", "kkt_update", "downdate",
-    "block_update", "rtn", "GPTQResult",
+    "block_update", "rtn", "GPTQResult", "grid_maxq",
+    "static_group_grids", "stored_codes",
 ]
 
 EPS_FLOOR = 2.0 ** -23      # damping floor: float32 machine epsilon
@@ -89,12 +99,24 @@ def hessian_from_sum(S, n: int) -> np.ndarray:
 # The b-bit affine quantizer: [derivation] section 1.1 and eq. (36)
 # ----------------------------------------------------------------------------
 
-def fit_grid(w, bits: int):
+def grid_maxq(bits: int, symmetric: bool = False) -> int:
+    """Largest unsigned code: 2^b - 1 for the min-max grid; 2^b - 2 for the
+    symmetric grid, whose 2^b - 1 levels -h..h (h = 2^(b-1) - 1) sit
+    symmetrically around an exact 0 (at b = 2 the ternary grid {-1, 0, +1})."""
+    return 2 ** bits - 2 if symmetric else 2 ** bits - 1
+
+
+def fit_grid(w, bits: int, symmetric: bool = False):
     """Min-max grid per row of w [m, k]: returns (scale float32 [m], zero [m]).
 
     Follows the rough min-max fit of [derivation] 1.1 with 15 -> 2^b - 1,
     widened to contain 0 (so the integer zero point represents 0 exactly) and
     with an all-zero range mapped to [-1, 1].  Evaluated in float32.
+
+    symmetric: the symmetric grid that [derivation] 1.1 names (its 8.4 notes
+    the signed code form): the range becomes [-a, a] with a = max |w|, the
+    levels are 2^b - 1 (maxq = 2^b - 2), so Delta = a / h and z = h with
+    h = 2^(b-1) - 1; the extremes +-a land exactly on the outer levels.
     """
     w = np.asarray(w)
     if w.ndim == 1:
@@ -102,6 +124,10 @@ def fit_grid(w, bits: int):
     maxq = np.float32(2 ** bits - 1)
     lo = np.minimum(w.min(axis=1), 0.0).astype(np.float32)
     hi = np.maximum(w.max(axis=1), 0.0).astype(np.float32)
+    if symmetric:
+        maxq = np.float32(grid_maxq(bits, True))
+        hi = np.maximum(-lo, hi)
+        lo = -hi
     flat = hi == lo
     lo = np.where(flat, np.float32(-1.0), lo).astype(np.float32)
     hi = np.where(flat, np.float32(1.0), hi).astype(np.float32)
@@ -111,13 +137,15 @@ def fit_grid(w, bits: int):
     return scale, zero.astype(np.int64)
 
 
-def encode(w, scale, zero, bits: int):
+def encode(w, scale, zero, bits: int, maxq=None):
     """c = clip(round(w/Delta) + z, 0, 2^b-1), q = Delta (c - z)   (eq. (36)).
 
     Returns (c int64, q float64, v float64) where v = w / Delta is the
     pre-rounding value (used to tell a genuine mismatch from a near-tie).
+    ``maxq`` overrides the top code (the symmetric grid stops at 2^b - 2).
     """
-    maxq = 2 ** bits - 1
+    if maxq is None:
+        maxq = 2 ** bits - 1
     scale = np.asarray(scale, dtype=np.float64)
     zero = np.asarray(zero, dtype=np.float64)
     v = np.asarray(w, dtype=np.float64) / scale
@@ -227,10 +255,11 @@ class GPTQResult:
     rho_perm: np.ndarray = field(repr=False, default=None)     # w - q
     zsrc_perm: np.ndarray = field(repr=False, default=None)    # -lo/Delta at fits
     packed: np.ndarray = field(repr=False, default=None)       # [m, words]
+    signed: bool = False        # symmetric grid: stored codes are c - z
 
 
 def quantize_columns(Wp, R, bits: int, group_size: int, blocksize: int,
-                     row_grid=None):
+                     row_grid=None, symmetric: bool = False, static_grid=None):
     """The blocked GPTQ column loop on a working copy already in processing
     order (dead columns zeroed).
 
@@ -238,13 +267,19 @@ def quantize_columns(Wp, R, bits: int, group_size: int, blocksize: int,
     starts a group, encode the column, rho = w - q, eta = rho / R_jj, update
     W[:, j:i2] -= eta R[j, j:i2]; then W[:, i2:] -= E R[i:i2, i2:].
 
+    symmetric: dynamic refits use the symmetric grid (see ``fit_grid``).
+    static_grid: (scales [m, n_s], zeros [m, n_s], gpos [d]) grids fixed in
+    advance (static groups, [derivation] 8.3): processing position j uses
+    column gpos[j] of them and nothing is refitted.
+
     Returns dict with codes, q, v, eta, rho (all [m, d], processing order),
     scales [m, n_g], zeros [m, n_g], zsrc [m, n_g] (the unrounded -lo/Delta).
     """
     W = np.array(Wp, dtype=np.float64, copy=True)
     R = np.asarray(R, dtype=np.float64)
     m, d = W.shape
-    if not check_group_layout(d, group_size, blocksize):
+    maxq = grid_maxq(bits, symmetric)
+    if static_grid is None and not check_group_layout(d, group_size, blocksize):
         raise ValueError("group_size / blocksize combination not supported")
     n_g = 1 if group_size == -1 else -(-d // group_size)
     codes = np.zeros((m, d), dtype=np.int64)
@@ -255,7 +290,12 @@ def quantize_columns(Wp, R, bits: int, group_size: int, blocksize: int,
     scales = np.zeros((m, n_g), dtype=np.float32)
     zeros = np.zeros((m, n_g), dtype=np.int64)
     zsrc = np.zeros((m, n_g))
-    if group_size == -1:
+    if static_grid is not None:
+        scales = np.array(static_grid[0], dtype=np.float32)
+        zeros = np.array(static_grid[1], dtype=np.int64)
+        gpos = np.asarray(static_grid[2], dtype=np.int64)
+        zsrc = zeros.astype(np.float64)     # zero points are given, not rounded
+    elif group_size == -1:
         scale, zero = row_grid
         scales[:, 0] = scale
         zeros[:, 0] = zero
@@ -263,14 +303,18 @@ def quantize_columns(Wp, R, bits: int, group_size: int, blocksize: int,
         i2 = min(i + blocksize, d)
         E = np.zeros((m, i2 - i))
         for j in range(i, i2):
-            if group_size > 0 and j % group_size == 0:
+            if static_grid is not None:
+                scale, zero = scales[:, gpos[j]], zeros[:, gpos[j]]
+            elif group_size > 0 and j % group_size == 0:
                 grp = W[:, j:min(j + group_size, d)]
-                scale, zero = fit_grid(grp, bits)
+                scale, zero = fit_grid(grp, bits, symmetric)
                 lo32 = np.minimum(grp.min(axis=1), 0.0).astype(np.float32)
                 zsrc[:, j // group_size] = (-lo32 / scale).astype(np.float64)
+                if symmetric:       # z = h is fixed: no rounding decides it
+                    zsrc[:, j // group_size] = zero
                 scales[:, j // group_size] = scale
                 zeros[:, j // group_size] = zero
-            c, q, v = encode(W[:, j], scale, zero, bits)
+            c, q, v = encode(W[:, j], scale, zero, bits, maxq)
             rho = W[:, j] - q
             eta = rho / R[j, j]
             W[:, j:i2] -= eta[:, None] * R[j, j:i2][None, :]
@@ -285,16 +329,38 @@ def quantize_columns(Wp, R, bits: int, group_size: int, blocksize: int,
                 zeros=zeros, zsrc=zsrc)
 
 
+def static_group_grids(W, bits: int, group_size: int, symmetric: bool = False):
+    """Grids of the static groups: fitted before GPTQ on the ORIGINAL
+    contiguous columns [G g, (G+1) g) of every row ([derivation] 8.3),
+    like the whole-row grid on the original row.  Returns ([m, n_g] scales,
+    [m, n_g] zeros)."""
+    W = np.asarray(W, dtype=np.float64)
+    m, d = W.shape
+    n_g = -(-d // group_size)
+    scales = np.zeros((m, n_g), dtype=np.float32)
+    zeros = np.zeros((m, n_g), dtype=np.int64)
+    for G in range(n_g):
+        scales[:, G], zeros[:, G] = fit_grid(W[:, G * group_size:(G + 1) * group_size],
+                                             bits, symmetric)
+    return scales, zeros
+
+
 def gptq_layer(W, S, n: int, bits: int = 4, group_size: int = -1,
                blocksize: int = 128, percdamp: float = 0.01,
                act_order: bool = False, damp_override=None,
-               fixed_grid=None) -> GPTQResult:
+               fixed_grid=None, symmetric: bool = False,
+               static_groups: bool = False) -> GPTQResult:
     """Quantize one linear layer W [m, d] given S = X X^T over n tokens.
 
     The steps and their order are the [derivation] section 10 pseudocode,
     extended to b bits, dynamic groups and act-order as its sections 8.3-8.4
     describe.  ``fixed_grid`` = (scale[m], zero[m]) replaces the row fit
-    (the section 11 worked example fixes its grid in advance).
+    (the section 11 worked example fixes its grid in advance); with
+    group_size > 0 it is (scales[m, n_g], zeros[m, n_g]) on the static
+    group layout.  ``symmetric`` selects the symmetric grid with signed
+    codes (``fit_grid``); ``static_groups`` fits the groups once on the
+    original contiguous columns ([derivation] 8.3) instead of refitting
+    them in processing order.
     """
     W = np.asarray(W, dtype=np.float64)
     m, d = W.shape
@@ -302,30 +368,57 @@ def gptq_layer(W, S, n: int, bits: int = 4, group_size: int = -1,
         raise ValueError("bits must be 2, 3, 4 or 8")
     if group_size == 0 or group_size < -1 or blocksize < 1:
         raise ValueError("bad group_size / blocksize")
+    if fixed_grid is not None and symmetric:
+        raise ValueError("a fixed grid carries its own zero points")
+    static = group_size > 0 and (static_groups or fixed_grid is not None)
     # whole-row grid is fitted on the original row, before the dead fix
     if group_size == -1:
-        row_grid = fixed_grid if fixed_grid is not None else fit_grid(W, bits)
+        row_grid = fixed_grid if fixed_grid is not None else fit_grid(W, bits, symmetric)
     else:
         row_grid = None
+    if static:
+        sg = fixed_grid if fixed_grid is not None else \
+            static_group_grids(W, bits, group_size, symmetric)
     H, perm, dead, damp = prepare(S, n, percdamp, act_order, damp_override)
     R, damp = factor(H, damp)
     Wp = W.copy()
     Wp[:, dead] = 0.0
     Wp = Wp[:, perm]
-    out = quantize_columns(Wp, R, bits, group_size, blocksize, row_grid)
+    if static:
+        out = quantize_columns(Wp, R, bits, group_size, blocksize,
+                               symmetric=symmetric,
+                               static_grid=(sg[0], sg[1], perm // group_size))
+    else:
+        out = quantize_columns(Wp, R, bits, group_size, blocksize, row_grid,
+                               symmetric=symmetric)
     codes = np.empty_like(out["codes"])
     codes[:, perm] = out["codes"]
     w_hat = np.empty((m, d))
     w_hat[:, perm] = out["q"]
     g_idx = np.zeros(d, dtype=np.int64)
-    if group_size > 0:
+    if static:
+        g_idx = np.arange(d) // group_size
+    elif group_size > 0:
         g_idx[perm] = np.arange(d) // group_size
-    return GPTQResult(codes=codes, scales=out["scales"], zeros=out["zeros"],
-                      g_idx=g_idx, w_hat=w_hat, perm=perm, dead=dead,
-                      damp=damp, R=R, codes_perm=out["codes"],
-                      v_perm=out["v"], eta_perm=out["eta"],
-                      rho_perm=out["rho"], zsrc_perm=out["zsrc"],
-                      packed=pack_codes(codes, bits))
+    res = GPTQResult(codes=codes, scales=out["scales"], zeros=out["zeros"],
+                     g_idx=g_idx, w_hat=w_hat, perm=perm, dead=dead,
+                     damp=damp, R=R, codes_perm=out["codes"],
+                     v_perm=out["v"], eta_perm=out["eta"],
+                     rho_perm=out["rho"], zsrc_perm=out["zsrc"],
+                     packed=pack_codes(codes, bits), signed=symmetric)
+    if symmetric:
+        res.packed = pack_codes(stored_codes(res, bits), bits)
+    return res
+
+
+def stored_codes(res: "GPTQResult", bits: int) -> np.ndarray:
+    """The codes as stored: unsigned c for the min-max and fixed grids; for
+    the symmetric grid the signed code c - z ([derivation] 8.4: the same
+    levels written as -h..h), kept as its low b bits (two's complement)."""
+    if not res.signed:
+        return res.codes
+    z = res.zeros[np.arange(res.codes.shape[0])[:, None], res.g_idx[None, :]]
+    return np.mod(res.codes - z, 2 ** bits)
 
 
 # ----------------------------------------------------------------------------

@@ -67,6 +67,32 @@ MUTATIONS = {
                  "stream[:, np.arange(d) * bits + (bits - 1 - k)] = (codes >> k) & 1"),
     # damping applied with the wrong sign
     "damp_sign": ("Hd = H + damp * eye", "Hd = H - damp * eye"),
+    # damping relative to the sum / the largest diagonal entry, or none
+    "damp_sum": ("damp = max(percdamp * float(np.mean(np.diag(H))), EPS_FLOOR)",
+                 "damp = max(percdamp * float(np.sum(np.diag(H))), EPS_FLOOR)"),
+    "damp_max": ("damp = max(percdamp * float(np.mean(np.diag(H))), EPS_FLOOR)",
+                 "damp = max(percdamp * float(np.max(np.diag(H))), EPS_FLOOR)"),
+    "damp_none": ("damp = max(percdamp * float(np.mean(np.diag(H))), EPS_FLOOR)",
+                  "damp = EPS_FLOOR"),
+    # wrong placeholder diagonal for never-seen features
+    "dead_diag_2": ("H[idx, idx] = 1.0", "H[idx, idx] = 2.0"),
+    # zero point floored instead of rounded
+    "zero_floor": ("zero = np.rint((-lo) / scale).astype(np.float32)",
+                   "zero = np.floor((-lo) / scale).astype(np.float32)"),
+    # symmetric grid with 2^b levels (an off-centre zero point)
+    "sym_levels": ("maxq = np.float32(grid_maxq(bits, True))",
+                   "maxq = np.float32(2 ** bits - 1)"),
+    # symmetric range taken from the positive side only
+    "sym_one_sided": ("hi = np.maximum(-lo, hi)", "hi = hi"),
+    # static group of position j taken in processing order, not floor(pi_j/g)
+    "static_gpos_processing": ("static_grid=(sg[0], sg[1], perm // group_size)",
+                               "static_grid=(sg[0], sg[1], np.arange(d) // group_size)"),
+    # static group ids permuted like dynamic ones
+    "static_gidx_permuted": ("        g_idx = np.arange(d) // group_size\n",
+                             "        g_idx[perm] = np.arange(d) // group_size\n"),
+    # symmetric codes stored unsigned
+    "signed_codes_unsigned": ("return np.mod(res.codes - z, 2 ** bits)",
+                              "return res.codes"),
 }
 
 
@@ -108,11 +134,19 @@ def run_battery(mod):
                               for g in (-1, 8) for a in (False, True)]
                 elif set(params) == {"bits", "group_size"}:
                     cases += [(fn, {"bits": 3, "group_size": 8})]
+                elif set(params) == {"act_order"}:
+                    cases += [(fn, {"act_order": a}) for a in (False, True)]
+                elif set(params) == {"seed", "symmetric"}:
+                    cases += [(fn, {"seed": 0, "symmetric": sy}) for sy in (False, True)]
+                else:
+                    raise AssertionError(f"battery cannot call {name}{tuple(params)}")
         for fn, kw in cases:
             try:
                 fn(**kw)
-            except Exception:       # noqa: BLE001 - any failure counts
-                failures += 1
+            except KeyboardInterrupt:
+                raise
+            except BaseException:   # noqa: BLE001 - any failure counts,
+                failures += 1       # pytest.fail / pytest.raises' Failed too
     finally:
         pins.orc, props.orc = saved
     return failures

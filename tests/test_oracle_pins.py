@@ -145,3 +145,45 @@ def test_sixteen_level_example_full_loop():
     # per-block loop with blocksize 1 (the tail update is then the lazy GEMM)
     res1 = orc.quantize_columns(W, res.R, 4, -1, 1, grid)
     np.testing.assert_allclose(res1["q"], g["W_hat"], atol=1e-12)
+
+
+def test_damping_example():
+    """[derivation] eq. (12) and the section 10 damping and dead-feature
+    lines on a hand-worked case: a never-seen feature gets the placeholder
+    diagonal 1 BEFORE the mean is taken; lambda = percdamp * mean(diag H)."""
+    g = load_golden("damping_example.json")
+    tok = np.array(g["tokens"])
+    S = orc.hessian_sum(tok)
+    n = tok.shape[0]
+    for act in (False, True):
+        H, perm, dead, damp = orc.prepare(S, n, g["percdamp"], act)
+        np.testing.assert_array_equal(dead, g["dead"])
+        assert abs(damp - g["damp"]) < 1e-15
+        np.testing.assert_allclose(np.diag(H)[np.argsort(perm)],
+                                   g["diag_after_dead_fix"], atol=1e-15)
+        if act:
+            np.testing.assert_array_equal(perm, g["perm_act_order"])
+            np.testing.assert_allclose(H, g["H_perm_act_order"], atol=1e-15)
+    # the damped matrix the factor inverts: R^T R (H + lambda I) = I
+    H, perm, dead, damp = orc.prepare(S, n, g["percdamp"], True)
+    R, used = orc.factor(H, damp)
+    assert used == damp
+    np.testing.assert_allclose(R.T @ R @ (np.array(g["H_perm_act_order"]) +
+                                          g["damp"] * np.eye(3)), np.eye(3),
+                               atol=1e-12)
+    c2 = g["second_case"]
+    _, _, _, damp2 = orc.prepare(np.diag(c2["S_diag"]), c2["n"], 0.01, False)
+    assert abs(damp2 - c2["damp"]) < 1e-15
+
+
+def test_zero_point_rounds_to_nearest():
+    """[derivation] 1.1: z = clip(round(-w_min / Delta), 0, 15).  The row
+    [-1.15, 1.85] has Delta = 3/15 = 0.2 and -w_min / Delta = 5.75, whose
+    nearest integer is 6 (flooring would give 5)."""
+    sc, z = orc.fit_grid(np.array([[-1.15, 1.85, 0.3]]), 4)
+    assert abs(float(sc[0]) - 0.2) < 1e-7
+    assert int(z[0]) == 6
+    # 0 is represented exactly and the extremes land within half a step
+    c, q, _ = orc.encode(np.array([0.0, -1.15, 1.85]), sc[0], z[0], 4)
+    assert q[0] == 0.0
+    assert abs(q[1] + 1.15) <= 0.1 + 1e-7 and abs(q[2] - 1.85) <= 0.1 + 1e-7

@@ -96,13 +96,13 @@ def test_block_formula_equals_sequential_and_lazy(seed):
     np.testing.assert_allclose(Wtail[:, b:], Wseq[:, b:], atol=1e-10)
 
 
-@pytest.mark.parametrize("seed", range(4))
-def _explicit_obs_gptq(W, H, perm, bits, group_size):
+def _explicit_obs_gptq(W, H, perm, bits, group_size, static=None):
     """The column loop by the route of [derivation] sections 4 and 6: for
     each column, the full OBS update (eq. (22)) with the current inverse
     Hessian of the free coordinates, then its rank-1 downdate (eq. (26)).
     No Cholesky factor and no blocking; dynamic groups fitted on the current
-    working row at each group start."""
+    working row at each group start.  ``static`` = (scales, zeros) [m, n_g]
+    on the original column layout: original column k uses group k // g."""
     Wp = np.array(W[:, perm], dtype=np.float64)
     m, d = Wp.shape
     G = np.linalg.inv(H)
@@ -111,7 +111,10 @@ def _explicit_obs_gptq(W, H, perm, bits, group_size):
     if group_size == -1:
         sc, z = orc.fit_grid(W, bits)
     for j in range(d):
-        if group_size > 0 and j % group_size == 0:
+        if static is not None:
+            k = perm[j]
+            sc, z = static[0][:, k // group_size], static[1][:, k // group_size]
+        elif group_size > 0 and j % group_size == 0:
             sc, z = orc.fit_grid(Wp[:, j:j + group_size], bits)
             scales.append(sc)
         c, q, _ = orc.encode(Wp[:, j], sc, z, bits)
@@ -380,3 +383,142 @@ def test_ragged_shapes_run():
     res = orc.gptq_layer(W, S, 50, bits=3, group_size=-1, blocksize=16)
     assert res.codes.shape == (3, 37) and res.packed.shape == (3, 4)
     assert res.codes.min() >= 0 and res.codes.max() <= 7
+
+
+# ----------------------------------------------------------------------------
+# Quantizer variants: symmetric (signed) grid, ternary, static groups
+# ----------------------------------------------------------------------------
+
+def test_symmetric_grid_hand_example():
+    """Symmetric 4-bit grid on [-0.33, 0.7, 0.12, -0.2]: a = 0.7, 15 levels
+    -7..7, Delta = a / 7 = 0.1, z = 7; w / Delta = -3.3, 7, 1.2, -2 round
+    to the signed codes -3, 7, 1, -2 (unsigned 4, 14, 8, 5)."""
+    w = np.array([[-0.33, 0.7, 0.12, -0.2]])
+    sc, z = orc.fit_grid(w, 4, symmetric=True)
+    assert abs(float(sc[0]) - 0.1) < 1e-7 and int(z[0]) == 7
+    c, q, _ = orc.encode(w[0], sc[0], z[0], 4, orc.grid_maxq(4, True))
+    np.testing.assert_array_equal(c - 7, [-3, 7, 1, -2])
+    np.testing.assert_allclose(q, [-0.3, 0.7, 0.1, -0.2], atol=1e-7)
+
+
+def test_ternary_grid_hand_example():
+    """[teardown] "extreme quantization": the ternary grid {-1, 0, +1} Delta
+    is the symmetric 2-bit grid.  A group of 8 with max |w| = 0.3 gets
+    Delta = 0.3; w / Delta rounds to -1, 0 or +1 only."""
+    w = np.array([[0.3, -0.1, 0.16, -0.2, 0.05, -0.3, 0.0, 0.29]])
+    sc, z = orc.fit_grid(w, 2, symmetric=True)
+    assert abs(float(sc[0]) - 0.3) < 1e-7 and int(z[0]) == 1
+    c, q, _ = orc.encode(w[0], sc[0], z[0], 2, orc.grid_maxq(2, True))
+    np.testing.assert_array_equal(c - 1, [1, 0, 1, -1, 0, -1, 0, 1])
+    assert set(np.round(q / 0.3, 6)) <= {-1.0, 0.0, 1.0}
+
+
+@pytest.mark.parametrize("bits", [2, 3, 4, 8])
+def test_symmetric_grid_is_odd_and_exact_at_extremes(bits):
+    """The symmetric grid maps -w to -q(w) (away from ties), represents 0
+    and +-max|w| exactly, and rounds every w in range within Delta / 2."""
+    rng = np.random.default_rng(bits)
+    w = rng.standard_normal((5, 33))
+    w[2] = 0.0
+    sc, z = orc.fit_grid(w, bits, symmetric=True)
+    mq = orc.grid_maxq(bits, True)
+    assert np.all(z == 2 ** (bits - 1) - 1)
+    for r in range(5):
+        c, q, v = orc.encode(w[r], sc[r], z[r], bits, mq)
+        cn, qn, _ = orc.encode(-w[r], sc[r], z[r], bits, mq)
+        far = np.abs(v - np.floor(v) - 0.5) > 1e-6
+        np.testing.assert_allclose(qn[far], -q[far], atol=0)
+        assert np.all(np.abs(q - w[r]) <= sc[r] / 2 * (1 + 1e-6))
+        if r != 2:
+            a = np.max(np.abs(w[r]))
+            k = int(np.argmax(np.abs(w[r])))
+            assert abs(abs(q[k]) - a) <= 1e-6 * a
+        c0, q0, _ = orc.encode(np.zeros(1), sc[r], z[r], bits, mq)
+        assert q0[0] == 0.0
+
+
+def test_symmetric_layer_codes_are_signed_two_complement():
+    rng = np.random.default_rng(8)
+    W, Xt = rand_layer(rng, 6, 20, 60)
+    S = orc.hessian_sum(Xt)
+    res = orc.gptq_layer(W, S, 60, bits=3, group_size=4, blocksize=8,
+                         symmetric=True)
+    signed = res.codes - 3
+    assert signed.min() >= -3 and signed.max() <= 3
+    unpacked = orc.unpack_codes(res.packed, 20, 3)
+    np.testing.assert_array_equal(np.where(unpacked >= 4, unpacked - 8, unpacked),
+                                  signed)
+    np.testing.assert_allclose(res.w_hat,
+                               res.scales[np.arange(6)[:, None], res.g_idx[None, :]]
+                               * signed, atol=1e-12)
+
+
+@pytest.mark.parametrize("act_order", [False, True])
+def test_static_groups_diagonal_H_is_rtn_on_original_groups(act_order):
+    """Static groups are fitted on the original contiguous columns, so with
+    a diagonal H (no compensation) the codes are the group-wise RTN codes
+    of the original layout whatever the processing order, and group_id is
+    the trivial k // g ([derivation] 8.3)."""
+    rng = np.random.default_rng(21)
+    m, d, g = 5, 24, 8
+    W = rng.standard_normal((m, d))
+    S = np.diag(rng.uniform(0.5, 3.0, d))
+    res = orc.gptq_layer(W, S, 10, bits=3, group_size=g, blocksize=8,
+                         act_order=act_order, static_groups=True)
+    np.testing.assert_array_equal(res.g_idx, np.arange(d) // g)
+    for G in range(d // g):
+        sc, z = orc.fit_grid(W[:, G * g:(G + 1) * g], 3)
+        c, _ = orc.rtn(W[:, G * g:(G + 1) * g], sc, z, 3)
+        np.testing.assert_array_equal(res.codes[:, G * g:(G + 1) * g], c)
+        np.testing.assert_array_equal(res.scales[:, G], sc)
+
+
+@pytest.mark.parametrize("seed", range(3))
+@pytest.mark.parametrize("symmetric", [False, True])
+def test_static_groups_equal_explicit_obs(seed, symmetric):
+    """With act-order, static groups (grid of processing position j =
+    group floor(pi_j / g) of the original layout) through the Cholesky /
+    lazy-block loop equal the explicit OBS + downdate route."""
+    rng = np.random.default_rng(300 + seed)
+    m, d, n, g = 6, 16, 60, 4
+    W, Xt = rand_layer(rng, m, d, n)
+    Xt[:, 7] *= 5.0
+    S = orc.hessian_sum(Xt)
+    res = orc.gptq_layer(W, S, n, bits=3, group_size=g, blocksize=3,
+                         act_order=True, static_groups=True, symmetric=symmetric)
+    H, perm, _, damp = orc.prepare(S, n, 0.01, True)
+    assert not np.array_equal(perm, np.arange(d))
+    grids = orc.static_group_grids(W, 3, g, symmetric)
+    np.testing.assert_array_equal(res.scales, grids[0])
+    codes = _explicit_static(W, H + damp * np.eye(d), perm, 3, g, grids,
+                             orc.grid_maxq(3, symmetric))
+    np.testing.assert_array_equal(res.codes_perm, codes)
+
+
+def _explicit_static(W, H, perm, bits, g, grids, maxq):
+    Wp = np.array(W[:, perm], dtype=np.float64)
+    m, d = Wp.shape
+    G = np.linalg.inv(H)
+    codes = np.zeros((m, d), dtype=np.int64)
+    for j in range(d):
+        k = perm[j]
+        c, q, _ = orc.encode(Wp[:, j], grids[0][:, k // g], grids[1][:, k // g],
+                             bits, maxq)
+        codes[:, j] = c
+        for r in range(m):
+            delta, _ = orc.obs_update(G, 0, Wp[r, j] - q[r])
+            Wp[r, j:] += delta
+        G = orc.downdate(G, 0)
+    return codes
+
+
+def test_static_groups_any_blocksize():
+    """Static grids are fixed in advance, so no (g, blocksize) rule applies
+    and every blocksize gives the same codes."""
+    rng = np.random.default_rng(31)
+    W, Xt = rand_layer(rng, 7, 40, 120, rank=10)
+    S = orc.hessian_sum(Xt)
+    outs = [orc.gptq_layer(W, S, 120, bits=4, group_size=12, blocksize=b,
+                           static_groups=True, act_order=True) for b in (1, 7, 128)]
+    for o in outs[1:]:
+        np.testing.assert_array_equal(o.codes, outs[0].codes)
