@@ -63,19 +63,27 @@ __global__ __launch_bounds__(1024) void prep_stats_kernel(
     __syncthreads();
   }
   if (threadIdx.x == 0) {
-    double damp = fmax(percdamp * (red[0] / double(d)), kEpsFloor);
+    const double mean = red[0] / double(d);
+    double damp = fmax(percdamp * mean, kEpsFloor);
     for (int a = 0; a < attempt; ++a) damp *= 10.0;
-    *damp_out = damp;
+    // a non-finite diagonal (NaN or inf) makes every pivot NaN, which the
+    // factor flags as not positive definite
+    *damp_out = isfinite(mean) ? damp : __builtin_nan("");
   }
 }
 
 // Stable descending order of the keys by rank counting:
 // rank(j) = #{k : key_k > key_j} + #{k < j : key_k == key_j}.
+// NaN keys (a non-finite statistic) are ordered after every number, among
+// themselves by index, so the ranks are always a permutation of 0..d-1 and
+// every later gather through perm stays in bounds; the factor then reports
+// the non-finite matrix as not positive definite.
 __global__ __launch_bounds__(256) void rank_sort_kernel(
     const double* __restrict__ keys, int64_t d, int32_t* __restrict__ perm) {
   __shared__ double tile[256];
   const int64_t j = int64_t(blockIdx.x) * 256 + threadIdx.x;
   const double kj = j < d ? keys[j] : 0.0;
+  const bool nj = kj != kj;
   int64_t rank = 0;
   for (int64_t t0 = 0; t0 < d; t0 += 256) {
     tile[threadIdx.x] = (t0 + threadIdx.x < d) ? keys[t0 + threadIdx.x] : 0.0;
@@ -83,7 +91,9 @@ __global__ __launch_bounds__(256) void rank_sort_kernel(
     const int lim = static_cast<int>(min<int64_t>(256, d - t0));
     for (int k = 0; k < lim; ++k) {
       const double kk = tile[k];
-      rank += (kk > kj) || (kk == kj && t0 + k < j);
+      const bool nk = kk != kk;
+      const bool same = nk == nj && (nk || kk == kj);
+      rank += (!nk && (nj || kk > kj)) || (same && t0 + k < j);
     }
     __syncthreads();
   }

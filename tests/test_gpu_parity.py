@@ -153,6 +153,43 @@ def test_factor_not_spd(dev):
     assert ei.value.status == gq.GPTQ_ERR_NOT_SPD
 
 
+def test_factor_nan_statistics_not_spd(dev):
+    """A NaN on the diagonal of S (a corrupt calibration batch): act-order
+    still yields a permutation (NaN keys last, by index) and the factor
+    reports not positive definite instead of reading out of bounds."""
+    import ctypes
+    d, n = 300, 1000
+    rng = np.random.default_rng(31)
+    A = rng.standard_normal((n, d)).astype(np.float32)
+    S_np = A.T @ A                                  # float32
+    S = torch.from_numpy(S_np).to(dev)
+    S[7, 7] = float("nan")
+    S[100, 100] = float("nan")
+    lib = gq.load_library()
+    R = torch.empty(d, d, dtype=torch.float32, device=dev)
+    perm = torch.full((d,), -1, dtype=torch.int32, device=dev)
+    dead = torch.empty(d, dtype=torch.uint8, device=dev)
+    ws = torch.empty(lib.gptq_factor_workspace_bytes(d), dtype=torch.uint8, device=dev)
+    damp = ctypes.c_float(0.0)
+    p = lambda t: ctypes.c_void_p(t.data_ptr())
+    st = ctypes.c_void_p(torch.cuda.current_stream(dev).cuda_stream)
+    rc = lib.gptq_cholesky_inverse(p(S), n, d, 0.01, 1, p(R), p(perm), p(dead),
+                                   ctypes.byref(damp), p(ws), ws.numel(), st)
+    torch.cuda.synchronize()
+    assert rc == gq.GPTQ_ERR_NOT_SPD
+    pv = perm.cpu().numpy()
+    np.testing.assert_array_equal(np.sort(pv), np.arange(d))
+    np.testing.assert_array_equal(pv[-2:], [7, 100])
+    diag = np.diag(S_np).astype(np.float64)
+    diag[[7, 100]] = -np.inf
+    np.testing.assert_array_equal(pv[:-2], np.argsort(-diag, kind="stable")[:-2])
+    W = synth.normal_weight(16, d, 0.02, 31, "nan/W", dev)
+    with pytest.raises(gq.GPTQError) as ei:
+        gq.gptq_quantize_layer(W, S, n, bits=4, group_size=-1, blocksize=128,
+                               percdamp=0.01, act_order=True)
+    assert ei.value.status == gq.GPTQ_ERR_NOT_SPD
+
+
 def test_factor_and_layer_on_user_stream(dev):
     """Part of the triangular inverse runs on the library's own stream, forked
     from the caller's stream and joined back into it.  On a caller stream
