@@ -59,7 +59,8 @@ __all__ = [
     "pack_codes", "unpack_codes", "layer_error", "proxy_loss",
     "obs_criterion", "obs_update", "kkt_update", "downdate",
     "block_update", "rtn", "GPTQResult", "grid_maxq",
-    "static_group_grids", "stored_codes",
+    "static_group_grids", "stored_codes", "dequantize", "dequant_matmul",
+    "bf16_round", "activate", "gptq_stack",
 ]
 
 EPS_FLOOR = 2.0 ** -23      # damping floor: float32 machine epsilon
@@ -453,6 +454,89 @@ def unpack_codes(packed, d: int, bits: int) -> np.ndarray:
         bit = (packed[:, p // 32] >> (p % 32).astype(np.uint64)) & np.uint64(1)
         codes |= bit.astype(np.int64) << k
     return codes
+
+
+# ----------------------------------------------------------------------------
+# Inference on the stored format: the dequantized matmul ([wiki] "inference":
+# the packed low-bit weights are dequantized inside the matmul kernel;
+# [derivation] 3.1 and 8.3: codes, a scale and zero per (row, group), and a
+# group id per column when groups and act-order meet)
+# ----------------------------------------------------------------------------
+
+def dequantize(packed, scales, zeros, g_idx, d: int, bits: int,
+               signed: bool = False) -> np.ndarray:
+    """W_hat[r][c] = Delta[r][g(c)] (c_rc - z[r][g(c)]) with g(c) = g_idx[c].
+
+    ``signed``: the stored codes are the low ``bits`` bits of c - z (the
+    symmetric grid); they are sign-extended and the zero point is 0."""
+    codes = unpack_codes(packed, d, bits)
+    scales = np.asarray(scales, dtype=np.float64)
+    zeros = np.asarray(zeros, dtype=np.float64)
+    g_idx = np.asarray(g_idx, dtype=np.int64)
+    rows = np.arange(codes.shape[0])[:, None]
+    if signed:
+        codes = np.where(codes >= 2 ** (bits - 1), codes - 2 ** bits, codes)
+        zeros = np.zeros_like(zeros)
+    return scales[rows, g_idx[None, :]] * (codes - zeros[rows, g_idx[None, :]])
+
+
+def dequant_matmul(x, packed, scales, zeros, g_idx, bits: int,
+                   signed: bool = False) -> np.ndarray:
+    """Y = x W_hat^T for token-major activations x [n, d]: the layer's
+    output on the quantized weights, in float64."""
+    x = np.asarray(x, dtype=np.float64)
+    W_hat = dequantize(packed, scales, zeros, g_idx, x.shape[1], bits, signed)
+    return x @ W_hat.T
+
+
+# ----------------------------------------------------------------------------
+# Layer by layer: [derivation] 3.2 steps 1-2 and 10 (capture each layer's
+# inputs, quantize it, check its reconstruction error, go on to the next);
+# [teardown] "layer-wise quantization".  Reading: the next layer's inputs are
+# the quantized layer's outputs (after an elementwise activation), stored as
+# bf16 like any captured activation.
+# ----------------------------------------------------------------------------
+
+def bf16_round(y) -> np.ndarray:
+    """Round to bfloat16 (8 significant bits, half to even), from float64
+    directly (one rounding)."""
+    y = np.asarray(y, dtype=np.float64)
+    mant, expo = np.frexp(y)                   # y = mant 2^expo, 0.5 <= |mant| < 1
+    return np.ldexp(np.rint(mant * 256.0) / 256.0, expo)
+
+
+def activate(y, activation: str) -> np.ndarray:
+    """The elementwise activation between layers: none, relu or silu."""
+    y = np.asarray(y, dtype=np.float64)
+    if activation == "relu":
+        return np.maximum(y, 0.0)
+    if activation == "silu":
+        return y / (1.0 + np.exp(-y))
+    if activation != "none":
+        raise ValueError(activation)
+    return y
+
+
+def gptq_stack(Ws, X0, layer_params, activation: str = "none"):
+    """Quantize a stack of linear layers in order.  Layer l sees the token-
+    major inputs X_l (X_0 given); its statistics, factor and loop are
+    ``gptq_layer``; its reconstruction error (1/N)||(W - W_hat) X||_F^2 is
+    reported; X_{l+1} = bf16(act(X_l W_hat_l^T)) from the stored format.
+    Returns (per-layer list of dicts with res / err / S / X, final X)."""
+    X = np.asarray(X0, dtype=np.float64)
+    out = []
+    for W, p in zip(Ws, layer_params):
+        W = np.asarray(W, dtype=np.float64)
+        n = X.shape[0]
+        S = hessian_sum(X)
+        res = gptq_layer(W, S, n, **p)
+        err = layer_error(W, res.w_hat, S, n)
+        zeros = np.zeros_like(res.zeros) if res.signed else res.zeros
+        Y = dequant_matmul(X, res.packed, res.scales, zeros, res.g_idx,
+                           p.get("bits", 4), res.signed)
+        out.append(dict(res=res, err=err, S=S, X=X))
+        X = bf16_round(activate(Y, activation))
+    return out, X
 
 
 # ----------------------------------------------------------------------------

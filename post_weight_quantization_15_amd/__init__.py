@@ -18,7 +18,8 @@ __all__ = [
     "GPTQError", "lib_path", "load_library", "gptq_hessian_accumulate",
     "gptq_cholesky_inverse", "gptq_quantize_layer", "gptq_workspace_bytes",
     "gptq_hessian_workspace_bytes", "gptq_factor_workspace_bytes",
-    "EXPORTED_SYMBOLS", "GPTQ_OK", "GPTQ_ERR_INVALID_ARG", "GPTQ_ERR_NOT_SPD",
+    "gptq_dequant_matmul", "gptq_quantize_stack",
+    "EXPORTED_SYMBOLS", "GRIDS", "ACTIVATIONS", "GPTQ_OK", "GPTQ_ERR_INVALID_ARG", "GPTQ_ERR_NOT_SPD",
     "GPTQ_ERR_WORKSPACE", "GPTQ_ERR_HIP",
 ]
 
@@ -29,7 +30,9 @@ EXPORTED_SYMBOLS = (
     "gptq_status_string", "gptq_hessian_workspace_bytes",
     "gptq_hessian_accumulate", "gptq_factor_workspace_bytes",
     "gptq_cholesky_inverse", "gptq_workspace_bytes", "gptq_quantize_layer",
+    "gptq_dequant_matmul", "gptq_stack_workspace_bytes", "gptq_quantize_stack",
 )
+ACTIVATIONS = {"none": 0, "relu": 1, "silu": 2}
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _LIB = None
@@ -42,10 +45,22 @@ class GPTQError(RuntimeError):
         super().__init__(f"{where}: {msg} (status {status})")
 
 
+GRIDS = {"minmax": 0, "symmetric": 1, "fixed": 2}
+
+
 class _Params(ctypes.Structure):
     _fields_ = [("bits", ctypes.c_int32), ("group_size", ctypes.c_int32),
                 ("blocksize", ctypes.c_int32), ("percdamp", ctypes.c_float),
-                ("act_order", ctypes.c_int32)]
+                ("act_order", ctypes.c_int32), ("grid", ctypes.c_int32),
+                ("static_groups", ctypes.c_int32), ("fixed_scales", ctypes.c_void_p),
+                ("fixed_zeros", ctypes.c_void_p)]
+
+
+class _StackLayer(ctypes.Structure):
+    _fields_ = [("W", ctypes.c_void_p), ("w_dtype", ctypes.c_int), ("m", ctypes.c_int64),
+                ("d", ctypes.c_int64), ("ldw", ctypes.c_int64), ("params", _Params),
+                ("qweight", ctypes.c_void_p), ("scales", ctypes.c_void_p),
+                ("zeros", ctypes.c_void_p), ("g_idx", ctypes.c_void_p)]
 
 
 def lib_path() -> str:
@@ -71,6 +86,15 @@ def load_library():
     lib.gptq_hessian_workspace_bytes.argtypes = [i64, i64]
     lib.gptq_hessian_accumulate.restype = ctypes.c_int
     lib.gptq_hessian_accumulate.argtypes = [vp, i64, vp, ctypes.c_int, i64, i64, vp, sz, vp]
+    lib.gptq_dequant_matmul.restype = ctypes.c_int
+    lib.gptq_dequant_matmul.argtypes = [vp, ctypes.c_int, i64, i64, i64, vp, vp, vp, vp,
+                                        i64, i32, i32, i32, vp, i64, vp]
+    sp = ctypes.POINTER(_StackLayer)
+    lib.gptq_stack_workspace_bytes.restype = sz
+    lib.gptq_stack_workspace_bytes.argtypes = [sp, i32, i64]
+    lib.gptq_quantize_stack.restype = ctypes.c_int
+    lib.gptq_quantize_stack.argtypes = [sp, i32, vp, i64, i32, vp,
+                                        ctypes.POINTER(ctypes.c_double), vp, sz, vp]
     lib.gptq_factor_workspace_bytes.restype = sz
     lib.gptq_factor_workspace_bytes.argtypes = [i64]
     lib.gptq_cholesky_inverse.restype = ctypes.c_int
@@ -109,9 +133,14 @@ def _dtype_code(t):
     raise TypeError(f"unsupported dtype {t.dtype}; use bfloat16 or float32")
 
 
-def _params(bits, group_size, blocksize, percdamp, act_order):
+def _params(bits, group_size, blocksize, percdamp, act_order, grid="minmax",
+            static_groups=False, fixed_scales=None, fixed_zeros=None):
+    if grid not in GRIDS:
+        raise ValueError(f"grid must be one of {sorted(GRIDS)}")
     return _Params(int(bits), int(group_size), int(blocksize), float(percdamp),
-                   int(bool(act_order)))
+                   int(bool(act_order)), GRIDS[grid], int(bool(static_groups)),
+                   fixed_scales.data_ptr() if fixed_scales is not None else None,
+                   fixed_zeros.data_ptr() if fixed_zeros is not None else None)
 
 
 def _check(status, where):
@@ -123,6 +152,31 @@ def _workspace(nbytes, device):
     return torch.empty(max(int(nbytes), 1), dtype=torch.uint8, device=device)
 
 
+def _row_stride(t, name):
+    """Leading dimension of a row-major [rows, cols] tensor with unit column
+    stride.  Rows that overlap (stride(0) < cols, e.g. an expanded view)
+    cannot be described by one leading dimension and are rejected."""
+    rows, cols = t.shape
+    if t.stride(1) != 1 and cols > 1:
+        raise ValueError(f"{name} must have unit column stride")
+    if rows > 1 and t.stride(0) < cols:
+        raise ValueError(f"{name} rows overlap (stride(0) = {t.stride(0)} < {cols})")
+    return t.stride(0) if rows > 1 else cols
+
+
+def _expect(t, name, dtype, shape, device):
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} must have shape {tuple(shape)}, got {tuple(t.shape)}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if t.device != device:
+        raise ValueError(f"{name} is on {t.device}, expected {device}")
+
+
 def gptq_hessian_workspace_bytes(d: int, n_tok: int) -> int:
     return int(_lib().gptq_hessian_workspace_bytes(d, n_tok))
 
@@ -132,25 +186,33 @@ def gptq_factor_workspace_bytes(d: int) -> int:
 
 
 def gptq_workspace_bytes(m, d, bits=4, group_size=-1, blocksize=128,
-                         percdamp=0.01, act_order=False, factor_inside=True) -> int:
-    p = _params(bits, group_size, blocksize, percdamp, act_order)
+                         percdamp=0.01, act_order=False, factor_inside=True,
+                         grid="minmax", static_groups=False, fixed_scales=None,
+                         fixed_zeros=None) -> int:
+    p = _params(bits, group_size, blocksize, percdamp, act_order, grid,
+                static_groups, fixed_scales, fixed_zeros)
     return int(_lib().gptq_workspace_bytes(m, d, ctypes.byref(p), int(factor_inside)))
 
 
 def gptq_hessian_accumulate(S: torch.Tensor, X: torch.Tensor, ws=None) -> torch.Tensor:
     """S [d, d] fp32 += X^T X for token-major X [n_tok, d] (bf16 or fp32)."""
+    if S.dim() != 2 or S.shape[0] != S.shape[1]:
+        raise ValueError("S must be a [d, d] tensor")
+    d = S.shape[0]
+    _expect(S, "S", torch.float32, (d, d), S.device)
+    if X.dim() != 2 or X.shape[1] != d:
+        raise ValueError("X must be [n_tok, d]")
+    if X.device != S.device:
+        raise ValueError("X and S must be on the same device")
+    ldx = _row_stride(X, "X")
+    dtc = _dtype_code(X)
     lib = _lib()
-    if S.dtype != torch.float32 or S.dim() != 2 or S.shape[0] != S.shape[1] \
-            or not S.is_contiguous():
-        raise ValueError("S must be a contiguous float32 [d, d] tensor")
-    if X.dim() != 2 or X.shape[1] != S.shape[0] or X.stride(1) != 1:
-        raise ValueError("X must be [n_tok, d] with unit column stride")
-    d, n_tok = S.shape[0], X.shape[0]
+    n_tok = X.shape[0]
     need = lib.gptq_hessian_workspace_bytes(d, n_tok)
     if ws is None or ws.numel() < need:
         ws = _workspace(need, S.device)
-    st = lib.gptq_hessian_accumulate(_dev_ptr(S), d, _dev_ptr(X), _dtype_code(X),
-                                     n_tok, max(X.stride(0), d), _dev_ptr(ws),
+    st = lib.gptq_hessian_accumulate(_dev_ptr(S), d, _dev_ptr(X), dtc,
+                                     n_tok, ldx, _dev_ptr(ws),
                                      ws.numel(), _stream(S.device))
     _check(st, "gptq_hessian_accumulate")
     return S
@@ -159,9 +221,12 @@ def gptq_hessian_accumulate(S: torch.Tensor, X: torch.Tensor, ws=None) -> torch.
 def gptq_cholesky_inverse(S: torch.Tensor, n: int, percdamp: float = 0.01,
                           act_order: bool = False, ws=None):
     """Returns (R [d, d] fp32 upper, perm [d] int32, dead [d] uint8, damp)."""
-    lib = _lib()
+    if S.dim() != 2 or S.shape[0] != S.shape[1]:
+        raise ValueError("S must be a [d, d] tensor")
     d = S.shape[0]
     dev = S.device
+    _expect(S, "S", torch.float32, (d, d), dev)
+    lib = _lib()
     R = torch.empty(d, d, dtype=torch.float32, device=dev)
     perm = torch.empty(d, dtype=torch.int32, device=dev)
     dead = torch.empty(d, dtype=torch.uint8, device=dev)
@@ -169,7 +234,7 @@ def gptq_cholesky_inverse(S: torch.Tensor, n: int, percdamp: float = 0.01,
     if ws is None or ws.numel() < need:
         ws = _workspace(need, dev)
     damp = ctypes.c_float(0.0)
-    st = lib.gptq_cholesky_inverse(_dev_ptr(S.contiguous()), int(n), d, float(percdamp),
+    st = lib.gptq_cholesky_inverse(_dev_ptr(S), int(n), d, float(percdamp),
                                    int(bool(act_order)), _dev_ptr(R), _dev_ptr(perm),
                                    _dev_ptr(dead), ctypes.byref(damp), _dev_ptr(ws),
                                    ws.numel(), _stream(dev))
@@ -181,21 +246,45 @@ def gptq_quantize_layer(W: torch.Tensor, S: torch.Tensor = None, n: int = 0,
                         bits: int = 4, group_size: int = -1, blocksize: int = 128,
                         percdamp: float = 0.01, act_order: bool = False,
                         R=None, perm=None, dead=None, want_w_hat: bool = False,
-                        ws=None) -> dict:
-    """Quantize W [m, d]; returns qweight, scales, zeros, g_idx (and w_hat)."""
-    lib = _lib()
-    if W.dim() != 2 or W.stride(1) != 1:
-        raise ValueError("W must be [m, d] with unit column stride")
+                        ws=None, grid: str = "minmax", static_groups: bool = False,
+                        fixed_scales=None, fixed_zeros=None) -> dict:
+    """Quantize W [m, d]; returns qweight, scales, zeros, g_idx (and w_hat).
+
+    grid: "minmax", "symmetric" (signed codes; ternary at bits=2) or
+    "fixed" (fixed_scales fp32 / fixed_zeros uint8, [m, n_g] on W's device).
+    static_groups: fit the groups on the original contiguous columns."""
+    if W.dim() != 2:
+        raise ValueError("W must be [m, d]")
     m, d = W.shape
     dev = W.device
-    p = _params(bits, group_size, blocksize, percdamp, act_order)
+    ldw = _row_stride(W, "W")
+    dtc = _dtype_code(W)
+    given = [t is not None for t in (R, perm, dead)]
+    if any(given) and not all(given):
+        raise ValueError("pass R, perm and dead together (or none of them)")
+    if all(given):
+        _expect(R, "R", torch.float32, (d, d), dev)
+        _expect(perm, "perm", torch.int32, (d,), dev)
+        _expect(dead, "dead", torch.uint8, (d,), dev)
+    else:
+        if S is None:
+            raise ValueError("S is required when no factor is given")
+        _expect(S, "S", torch.float32, (d, d), dev)
+    ng = 1 if group_size == -1 else -(-d // group_size)
+    if grid == "fixed":
+        _expect(fixed_scales, "fixed_scales", torch.float32, (m, ng), dev)
+        _expect(fixed_zeros, "fixed_zeros", torch.uint8, (m, ng), dev)
+    elif fixed_scales is not None or fixed_zeros is not None:
+        raise ValueError("fixed_scales / fixed_zeros need grid='fixed'")
+    lib = _lib()
+    p = _params(bits, group_size, blocksize, percdamp, act_order, grid,
+                static_groups, fixed_scales, fixed_zeros)
     factor_inside = R is None
     need = lib.gptq_workspace_bytes(m, d, ctypes.byref(p), int(factor_inside))
     if need == 0:
         raise GPTQError(GPTQ_ERR_INVALID_ARG, "gptq_workspace_bytes")
     if ws is None or ws.numel() < need:
         ws = _workspace(need, dev)
-    ng = 1 if group_size == -1 else -(-d // group_size)
     words = -(-d * bits // 32)
     out = dict(
         qweight=torch.empty(m, words, dtype=torch.int32, device=dev),
@@ -205,8 +294,8 @@ def gptq_quantize_layer(W: torch.Tensor, S: torch.Tensor = None, n: int = 0,
     )
     w_hat = torch.empty(m, d, dtype=torch.float32, device=dev) if want_w_hat else None
     st = lib.gptq_quantize_layer(
-        _dev_ptr(W), _dtype_code(W), m, d, max(W.stride(0), d),
-        _dev_ptr(S.contiguous()) if S is not None else None, int(n), ctypes.byref(p),
+        _dev_ptr(W), dtc, m, d, ldw,
+        _dev_ptr(S) if S is not None and not all(given) else None, int(n), ctypes.byref(p),
         _dev_ptr(R), _dev_ptr(perm), _dev_ptr(dead),
         _dev_ptr(out["qweight"]), _dev_ptr(out["scales"]), _dev_ptr(out["zeros"]),
         _dev_ptr(out["g_idx"]), _dev_ptr(w_hat), _dev_ptr(ws), ws.numel(), _stream(dev))
@@ -214,3 +303,97 @@ def gptq_quantize_layer(W: torch.Tensor, S: torch.Tensor = None, n: int = 0,
     if want_w_hat:
         out["w_hat"] = w_hat
     return out
+
+
+def gptq_dequant_matmul(X: torch.Tensor, qweight: torch.Tensor, scales: torch.Tensor,
+                        zeros: torch.Tensor, g_idx: torch.Tensor, bits: int,
+                        group_size: int, signed: bool = False, Y=None) -> torch.Tensor:
+    """Y [n, m] fp32 = X W_hat^T for bf16 activations X [n, d] and the stored
+    format of gptq_quantize_layer (qweight, scales, zeros, g_idx)."""
+    if X.dim() != 2:
+        raise ValueError("X must be [n, d]")
+    n, d = X.shape
+    m = qweight.shape[0]
+    dev = X.device
+    if X.dtype != torch.bfloat16:
+        raise TypeError("X must be bfloat16")
+    ldx = _row_stride(X, "X")
+    words = -(-d * bits // 32)
+    ng = 1 if group_size == -1 else -(-d // group_size)
+    if qweight.dtype not in (torch.int32, torch.uint32):
+        raise TypeError("qweight must be int32/uint32")
+    if tuple(qweight.shape) != (m, words) or not qweight.is_contiguous():
+        raise ValueError(f"qweight must be contiguous [{m}, {words}]")
+    _expect(scales, "scales", torch.float32, (m, ng), dev)
+    _expect(zeros, "zeros", torch.uint8, (m, ng), dev)
+    _expect(g_idx, "g_idx", torch.int32, (d,), dev)
+    if qweight.device != dev:
+        raise ValueError("qweight must be on X's device")
+    if Y is None:
+        Y = torch.empty(n, m, dtype=torch.float32, device=dev)
+    else:
+        _expect(Y, "Y", torch.float32, (n, m), dev)
+    st = _lib().gptq_dequant_matmul(_dev_ptr(X), GPTQ_BF16, n, d, ldx, _dev_ptr(qweight),
+                                    _dev_ptr(scales), _dev_ptr(zeros), _dev_ptr(g_idx),
+                                    m, int(bits), int(group_size), int(bool(signed)),
+                                    _dev_ptr(Y), m, _stream(dev))
+    _check(st, "gptq_dequant_matmul")
+    return Y
+
+
+def gptq_quantize_stack(Ws, X: torch.Tensor, params, activation: str = "none",
+                        ws=None) -> dict:
+    """Quantize the linear layers Ws[0], Ws[1], ... in order, each on the
+    bf16 outputs of the quantized layer before it (X feeds the first).
+    params: one dict of gptq_quantize_layer settings per layer (or one dict
+    for all).  Returns {"layers": [outputs per layer], "layer_err": [floats],
+    "X_out": bf16 [n, m_last] (the next layer's inputs)}."""
+    if activation not in ACTIVATIONS:
+        raise ValueError(f"activation must be one of {sorted(ACTIVATIONS)}")
+    if isinstance(params, dict):
+        params = [params] * len(Ws)
+    if len(params) != len(Ws) or not Ws:
+        raise ValueError("one params dict per layer")
+    if X.dim() != 2 or X.dtype != torch.bfloat16 or not X.is_contiguous():
+        raise ValueError("X must be a contiguous bf16 [n, d] tensor")
+    dev = X.device
+    n = X.shape[0]
+    arr = (_StackLayer * len(Ws))()
+    outs = []
+    for i, (W, p) in enumerate(zip(Ws, params)):
+        if W.dim() != 2 or W.device != dev:
+            raise ValueError("each W must be [m, d] on X's device")
+        m, d = W.shape
+        ldw = _row_stride(W, "W")
+        g = p.get("group_size", -1)
+        bits = p.get("bits", 4)
+        ng = 1 if g == -1 else -(-d // g)
+        o = dict(qweight=torch.empty(m, -(-d * bits // 32), dtype=torch.int32, device=dev),
+                 scales=torch.empty(m, ng, dtype=torch.float32, device=dev),
+                 zeros=torch.empty(m, ng, dtype=torch.uint8, device=dev),
+                 g_idx=torch.empty(d, dtype=torch.int32, device=dev))
+        outs.append(o)
+        grid = p.get("grid", "minmax")
+        fs, fz = p.get("fixed_scales"), p.get("fixed_zeros")
+        if grid == "fixed":
+            _expect(fs, "fixed_scales", torch.float32, (m, ng), dev)
+            _expect(fz, "fixed_zeros", torch.uint8, (m, ng), dev)
+        pp = _params(bits, g, p.get("blocksize", 128), p.get("percdamp", 0.01),
+                     p.get("act_order", False), grid, p.get("static_groups", False),
+                     fs, fz)
+        arr[i] = _StackLayer(W.data_ptr(), _dtype_code(W), m, d, ldw, pp,
+                             o["qweight"].data_ptr(), o["scales"].data_ptr(),
+                             o["zeros"].data_ptr(), o["g_idx"].data_ptr())
+    lib = _lib()
+    need = lib.gptq_stack_workspace_bytes(arr, len(Ws), n)
+    if need == 0:
+        raise GPTQError(GPTQ_ERR_INVALID_ARG, "gptq_stack_workspace_bytes")
+    if ws is None or ws.numel() < need:
+        ws = _workspace(need, dev)
+    X_out = torch.empty(n, Ws[-1].shape[0], dtype=torch.bfloat16, device=dev)
+    errs = (ctypes.c_double * len(Ws))()
+    st = lib.gptq_quantize_stack(arr, len(Ws), _dev_ptr(X), n, ACTIVATIONS[activation],
+                                 _dev_ptr(X_out), errs, _dev_ptr(ws), ws.numel(),
+                                 _stream(dev))
+    _check(st, "gptq_quantize_stack")
+    return dict(layers=outs, layer_err=[float(e) for e in errs], X_out=X_out)

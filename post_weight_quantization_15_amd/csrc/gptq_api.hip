@@ -26,6 +26,12 @@ bool groups_fit_blocks(int64_t d, int64_t g, int64_t b) {
   return true;
 }
 
+// Groups fitted before the loop (static or caller-given grids) rather than
+// refitted in processing order.
+bool static_grids(const gptq_params* p) {
+  return p->group_size > 0 && (p->static_groups == 1 || p->grid == GPTQ_GRID_FIXED);
+}
+
 bool valid_params(const gptq_params* p, int64_t d) {
   if (!p) return false;
   if (!(p->bits == 2 || p->bits == 3 || p->bits == 4 || p->bits == 8)) return false;
@@ -33,7 +39,14 @@ bool valid_params(const gptq_params* p, int64_t d) {
   if (p->blocksize < 1) return false;
   if (!(p->percdamp >= 0.0f) || !std::isfinite(p->percdamp)) return false;
   if (p->act_order != 0 && p->act_order != 1) return false;
-  return groups_fit_blocks(d, p->group_size, p->blocksize);
+  if (p->grid != GPTQ_GRID_MINMAX && p->grid != GPTQ_GRID_SYMMETRIC &&
+      p->grid != GPTQ_GRID_FIXED)
+    return false;
+  if (p->static_groups != 0 && p->static_groups != 1) return false;
+  const bool fixed = p->grid == GPTQ_GRID_FIXED;
+  if (fixed != (p->fixed_scales != nullptr) || fixed != (p->fixed_zeros != nullptr))
+    return false;
+  return static_grids(p) || groups_fit_blocks(d, p->group_size, p->blocksize);
 }
 
 // Internal block width of the column loop: the requested block size when it
@@ -43,7 +56,9 @@ bool valid_params(const gptq_params* p, int64_t d) {
 int internal_block(int64_t d, const gptq_params* p) {
   if (p->blocksize <= kChainMaxBlock) return p->blocksize;
   for (int bi = kChainMaxBlock; bi >= 1; --bi)
-    if (p->blocksize % bi == 0 && groups_fit_blocks(d, p->group_size, bi)) return bi;
+    if (p->blocksize % bi == 0 &&
+        (static_grids(p) || groups_fit_blocks(d, p->group_size, bi)))
+      return bi;
   return 1;
 }
 
@@ -140,10 +155,21 @@ gptq_status enqueue_columns(const void* W, gptq_dtype w_dtype, int64_t m,
                             int32_t* g_idx, float* w_hat, hipStream_t st) {
   gptq_status s;
   const int64_t gsize = p->group_size;
-  // whole-row grid on the original row, before dead columns are zeroed
-  if (gsize == -1 &&
-      (s = launch_fit_rows(W, w_dtype, m, d, ldw, p->bits, q.scalesP, q.zerosP, st)) != GPTQ_OK)
-    return s;
+  const bool sym = p->grid == GPTQ_GRID_SYMMETRIC;
+  const bool stat = static_grids(p);
+  const float maxq = static_cast<float>((1 << p->bits) - (sym ? 2 : 1));
+  // grids fixed before the loop: given, or fitted on the original weights
+  // (the whole row, or the static groups) before dead columns are zeroed
+  if (p->grid == GPTQ_GRID_FIXED) {
+    const int64_t ng = gsize > 0 ? (d + gsize - 1) / gsize : 1;
+    if ((s = launch_grid_in(p->fixed_scales, p->fixed_zeros, m, ng, q.scalesP,
+                            q.zerosP, st)) != GPTQ_OK)
+      return s;
+  } else if (gsize == -1 || stat) {
+    if ((s = launch_fit_grids(W, w_dtype, m, d, ldw, gsize == -1 ? d : gsize, maxq,
+                              sym, q.scalesP, q.zerosP, st)) != GPTQ_OK)
+      return s;
+  }
   if ((s = launch_init_work(W, w_dtype, m, d, ldw, pu, du, q.WT, q.pinv, st)) != GPTQ_OK)
     return s;
   const int bi = internal_block(d, p);
@@ -152,26 +178,99 @@ gptq_status enqueue_columns(const void* W, gptq_dtype w_dtype, int64_t m,
   // earlier residuals to its own columns, and one update per batch carries
   // the whole batch to the columns after it (the same sums regrouped, as
   // lazy batching itself is).  Batches need full 128-column blocks and no
-  // group reaching past its block, whose fit would read columns of the
-  // batch that have not received the batch's residuals yet.
-  const bool batch = bi == kChainMaxBlock && (gsize == -1 || bi % gsize == 0);
+  // dynamic group reaching past its block, whose fit would read columns of
+  // the batch that have not received the batch's residuals yet.
+  const bool batch = bi == kChainMaxBlock && (gsize == -1 || stat || bi % gsize == 0);
   const int nb = batch ? kLazyBatch : 1;
+  ChainArgs a{};
+  a.WT = q.WT;
+  a.m = m;
+  a.d = d;
+  a.RL = q.RbT;
+  a.bi = bi;
+  a.maxq = maxq;
+  a.gsize = gsize;
+  a.fs = stat ? -1 : (gsize == -1 ? 0 : 1);
+  a.sym = sym;
+  a.sgn = sym;
+  a.cmask = (1 << p->bits) - 1;
+  a.perm = pu;
+  a.scalesP = q.scalesP;
+  a.zerosP = q.zerosP;
+  a.codesP = q.codesP;
+  a.R = Ru;
+  a.Esb = q.E;
   for (int64_t s0 = 0; s0 < d; s0 += int64_t(nb) * bi) {
     int64_t i0 = s0;
     for (int j = 0; j < nb && i0 < d; ++j, i0 += bi) {
-      const int bw = static_cast<int>(std::min<int64_t>(bi, d - i0));
-      if ((s = launch_chain(q.WT, m, d, q.RbT, i0, bw, bi, p->bits, gsize,
-                            q.scalesP, q.zerosP, q.codesP, q.E + (i0 - s0) * m, Ru,
-                            s0, q.E, st)) != GPTQ_OK)
-        return s;
+      a.i0 = i0;
+      a.bw = static_cast<int>(std::min<int64_t>(bi, d - i0));
+      a.E = q.E + (i0 - s0) * m;
+      a.sb0 = s0;
+      a.kn = static_cast<int>(i0 - s0);
+      if ((s = launch_chain(a, st)) != GPTQ_OK) return s;
     }
     const int kw = static_cast<int>(std::min<int64_t>(int64_t(nb) * bi, d - s0));
     if ((s = launch_lazy_update(q.WT, m, d, Ru, s0, kw, q.E, st)) != GPTQ_OK)
       return s;
   }
-  return launch_outputs(m, d, p->bits, static_cast<int>(gsize), q.codesP,
-                        q.scalesP, q.zerosP, q.pinv, q.codesO, qweight, scales,
-                        zeros, g_idx, w_hat, st);
+  return launch_outputs(m, d, p->bits, static_cast<int>(gsize), sym, stat,
+                        q.codesP, q.scalesP, q.zerosP, q.pinv, q.codesO,
+                        qweight, scales, zeros, g_idx, w_hat, st);
+}
+
+constexpr int64_t kMaxStackTokens = int64_t(65535) * 8;   // dequant grid.y
+
+struct StackWs {
+  float* S;
+  void* hws;
+  size_t hws_bytes;
+  void* qws;
+  size_t qws_bytes;
+  float* w_hat;
+  uint16_t* buf[2];
+  double* part;
+  double* errs;
+};
+
+bool valid_stack(const gptq_stack_layer* L, int32_t nl, int64_t n_tok) {
+  if (!L || nl < 1 || n_tok < 1 || n_tok > kMaxStackTokens) return false;
+  for (int32_t l = 0; l < nl; ++l) {
+    const gptq_stack_layer& a = L[l];
+    if (!a.W || a.m <= 0 || a.d <= 0 || a.m > kMaxDim || a.d > kMaxDim || a.ldw < a.d ||
+        !valid_dtype(a.w_dtype) || !valid_params(&a.params, a.d) || !a.qweight ||
+        !a.scales || !a.zeros || !a.g_idx)
+      return false;
+    if (l > 0 && a.d != L[l - 1].m) return false;
+  }
+  return true;
+}
+
+StackWs carve_stack_ws(Carver& c, const gptq_stack_layer* L, int32_t nl, int64_t n) {
+  int64_t dmax = 0, mmax = 0, wmax = 0;
+  size_t hb = 0, qb = 0, pc = 0;
+  for (int32_t l = 0; l < nl; ++l) {
+    dmax = std::max(dmax, L[l].d);
+    mmax = std::max(mmax, L[l].m);
+    wmax = std::max(wmax, L[l].m * L[l].d);
+    hb = std::max(hb, hessian_ws_bytes(L[l].d, n));
+    Carver q(nullptr);
+    carve_quant_ws(q, L[l].m, L[l].d, &L[l].params, true);
+    qb = std::max(qb, q.bytes());
+    pc = std::max(pc, layer_error_part_count(L[l].m, L[l].d));
+  }
+  StackWs w{};
+  w.S = c.take<float>(size_t(dmax) * size_t(dmax));
+  w.hws = c.take<char>(hb);
+  w.hws_bytes = hb;
+  w.qws = c.take<char>(qb);
+  w.qws_bytes = qb;
+  w.w_hat = c.take<float>(size_t(wmax));
+  w.buf[0] = c.take<uint16_t>(size_t(n) * size_t(mmax));
+  w.buf[1] = c.take<uint16_t>(size_t(n) * size_t(mmax));
+  w.part = c.take<double>(pc);
+  w.errs = c.take<double>(size_t(nl));
+  return w;
 }
 
 }  // namespace
@@ -208,6 +307,80 @@ gptq_status gptq_hessian_accumulate(float* S, int64_t d, const void* X,
   if (ws_bytes < need || (need > 0 && !ws)) return GPTQ_ERR_WORKSPACE;
   return launch_hessian(S, d, X, x_dtype, n_tok, ldx, ws,
                         static_cast<hipStream_t>(stream));
+}
+
+gptq_status gptq_dequant_matmul(const void* X, gptq_dtype x_dtype, int64_t n,
+                                int64_t d, int64_t ldx, const uint32_t* qweight,
+                                const float* scales, const uint8_t* zeros,
+                                const int32_t* g_idx, int64_t m, int32_t bits,
+                                int32_t group_size, int32_t signed_codes,
+                                float* Y, int64_t ldy, void* stream) {
+  if (x_dtype != GPTQ_BF16 || n < 0 || d <= 0 || m <= 0 || d > kMaxDim ||
+      ldx < d || ldy < m || !(bits == 2 || bits == 3 || bits == 4 || bits == 8) ||
+      !(group_size == -1 || group_size > 0) ||
+      (signed_codes != 0 && signed_codes != 1))
+    return GPTQ_ERR_INVALID_ARG;
+  if (n > 0 && (!X || !qweight || !scales || !zeros || !g_idx || !Y))
+    return GPTQ_ERR_INVALID_ARG;
+  const int64_t ng = group_size > 0 ? (d + group_size - 1) / group_size : 1;
+  if (n > int64_t(65535) * 8) return GPTQ_ERR_INVALID_ARG;
+  return launch_dequant_matmul(static_cast<const uint16_t*>(X), ldx, n, qweight, m,
+                               d, bits, scales, zeros, ng, g_idx, signed_codes, Y,
+                               ldy, 0, 0, static_cast<hipStream_t>(stream));
+}
+
+size_t gptq_stack_workspace_bytes(const gptq_stack_layer* layers, int32_t n_layers,
+                                  int64_t n_tok) {
+  if (!layers || n_layers < 1 || n_tok < 1) return 0;
+  for (int32_t l = 0; l < n_layers; ++l) {
+    if (layers[l].m <= 0 || layers[l].d <= 0 || !valid_params(&layers[l].params, layers[l].d))
+      return 0;
+  }
+  Carver c(nullptr);
+  carve_stack_ws(c, layers, n_layers, n_tok);
+  return c.bytes();
+}
+
+gptq_status gptq_quantize_stack(const gptq_stack_layer* layers, int32_t n_layers,
+                                const void* X_in, int64_t n_tok, int32_t activation,
+                                void* X_out, double* layer_err, void* ws,
+                                size_t ws_bytes, void* stream) {
+  if (!valid_stack(layers, n_layers, n_tok) || !X_in || !X_out ||
+      activation < GPTQ_ACT_NONE || activation > GPTQ_ACT_SILU)
+    return GPTQ_ERR_INVALID_ARG;
+  Carver c(ws);
+  const StackWs w = carve_stack_ws(c, layers, n_layers, n_tok);
+  if (!ws || ws_bytes < c.bytes()) return GPTQ_ERR_WORKSPACE;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  gptq_status s;
+  for (int32_t l = 0; l < n_layers; ++l) {
+    const gptq_stack_layer& a = layers[l];
+    const void* Xc = l == 0 ? X_in : w.buf[(l - 1) & 1];
+    void* Xn = l == n_layers - 1 ? X_out : w.buf[l & 1];
+    // statistics of this layer's inputs (the previous quantized layer's
+    // outputs after the activation)
+    if ((s = launch_zero_f32(w.S, a.d * a.d, st)) != GPTQ_OK) return s;
+    if ((s = launch_hessian(w.S, a.d, Xc, GPTQ_BF16, n_tok, a.d, w.hws, st)) != GPTQ_OK)
+      return s;
+    if ((s = gptq_quantize_layer(a.W, a.w_dtype, a.m, a.d, a.ldw, w.S, n_tok, &a.params,
+                                 nullptr, nullptr, nullptr, a.qweight, a.scales, a.zeros,
+                                 a.g_idx, w.w_hat, w.qws, w.qws_bytes, stream)) != GPTQ_OK)
+      return s;
+    if ((s = launch_layer_error(a.W, a.w_dtype, a.ldw, w.w_hat, w.S, a.m, a.d, n_tok,
+                                w.part, w.errs + l, st)) != GPTQ_OK)
+      return s;
+    const int64_t ng = a.params.group_size > 0 ? (a.d + a.params.group_size - 1) / a.params.group_size : 1;
+    if ((s = launch_dequant_matmul(static_cast<const uint16_t*>(Xc), a.d, n_tok, a.qweight,
+                                   a.m, a.d, a.params.bits, a.scales, a.zeros, ng, a.g_idx,
+                                   a.params.grid == GPTQ_GRID_SYMMETRIC, Xn, a.m, 1,
+                                   activation, st)) != GPTQ_OK)
+      return s;
+  }
+  if (layer_err)
+    GPTQ_CHECK_HIP(hipMemcpyAsync(layer_err, w.errs, sizeof(double) * size_t(n_layers),
+                                  hipMemcpyDeviceToHost, st));
+  GPTQ_CHECK_HIP(hipStreamSynchronize(st));
+  return GPTQ_OK;
 }
 
 size_t gptq_factor_workspace_bytes(int64_t d) {

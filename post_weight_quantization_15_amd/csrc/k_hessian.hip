@@ -43,7 +43,6 @@ constexpr int kCUs = 256;                      // MI355X compute units
 constexpr int kXcd = 8;                        // accelerator dies, own L2 each
 constexpr int kRegB = 8;                       // work order: blocks of 8x8 super-tiles
 constexpr int64_t kMaxChain = 2048;            // steps per fp32 running sum (see plan_splits)
-constexpr double kMaxPartBytes = 16.0 * (1 << 30);
 
 __host__ __device__ inline int64_t upper_tiles(int64_t nt) { return nt * (nt + 1) / 2; }
 
@@ -611,8 +610,9 @@ struct SplitPlan {
 // partial tiles cost a write and a read of 256 KiB per item.  Each split is
 // one fp32 running sum per entry; splits of at most kMaxChain steps bound its
 // rounding error (~steps * 2^-24 relative), as long as the partial tiles fit
-// in kMaxPartBytes.
-SplitPlan plan_splits(int64_t d, int64_t n_tok) {
+// in max_part bytes.  Plans whose partial tiles exceed max_part are never
+// chosen (one split needs none).
+SplitPlan plan_splits(int64_t d, int64_t n_tok, double max_part) {
   const int64_t nt = (d + kSup - 1) / kSup;
   const int64_t ntiles = upper_tiles(nt);
   const int64_t steps = (n_tok + kStep - 1) / kStep;
@@ -624,13 +624,14 @@ SplitPlan plan_splits(int64_t d, int64_t n_tok) {
   const double part_item = 4.0 * kSubElems * 4.0;
   int64_t min_split = 1;
   while (min_split < max_split && (steps + min_split - 1) / min_split > kMaxChain &&
-         double(min_split + 1) * double(ntiles) * part_item <= kMaxPartBytes)
+         double(min_split + 1) * double(ntiles) * part_item <= max_part)
     ++min_split;
   for (int64_t ns = min_split; ns <= max_split; ++ns) {
     // an even step count per split keeps every split but the last on the
     // unmasked path
     const int64_t per = ((steps + ns - 1) / ns + 1) & ~int64_t(1);
     const int64_t nsr = (steps + per - 1) / per;
+    if (nsr > 1 && double(nsr) * double(ntiles) * part_item > max_part) continue;
     const int64_t rounds = (ntiles * nsr + kCUs - 1) / kCUs;
     const double t = double(rounds) * double(per) * t_step +
                      (nsr > 1 ? 2.0 * double(nsr * ntiles) * 4.0 * kSubElems * 4.0 * t_byte : 0.0);
@@ -644,9 +645,9 @@ SplitPlan plan_splits(int64_t d, int64_t n_tok) {
 
 }  // namespace
 
-size_t hessian_ws_bytes(int64_t d, int64_t n_tok) {
+size_t hessian_ws_bytes(int64_t d, int64_t n_tok, double max_part) {
   if (d <= 0 || n_tok <= 0) return 0;
-  const SplitPlan p = plan_splits(d, n_tok);
+  const SplitPlan p = plan_splits(d, n_tok, max_part);
   if (p.nsplit <= 1) return 0;
   const int64_t nt = (d + kSup - 1) / kSup;
   return align_up(size_t(p.nsplit) * size_t(upper_tiles(nt)) * 4 * kSubElems * sizeof(float));
@@ -663,7 +664,7 @@ bool mfma_path_ok(int64_t d, const void* X, gptq_dtype dt, int64_t ldx) {
 
 gptq_status launch_hessian(float* S, int64_t d, const void* X, gptq_dtype dt,
                            int64_t n_tok, int64_t ldx, void* ws,
-                           hipStream_t st) {
+                           hipStream_t st, double max_part) {
   if (n_tok == 0) return GPTQ_OK;
   if (!mfma_path_ok(d, X, dt, ldx)) {
     const int nt64 = static_cast<int>((d + 63) / 64);
@@ -678,7 +679,7 @@ gptq_status launch_hessian(float* S, int64_t d, const void* X, gptq_dtype dt,
     return GPTQ_OK;
   }
   const int nt = static_cast<int>((d + kSup - 1) / kSup);
-  const SplitPlan p = plan_splits(d, n_tok);
+  const SplitPlan p = plan_splits(d, n_tok, max_part);
   const int64_t per_xcd = (upper_tiles(nt) * p.nsplit + kXcd - 1) / kXcd;
   const dim3 grid(static_cast<unsigned>(kXcd * per_xcd));
   hessian_bf16_kernel<true><<<grid, kThreads, 0, st>>>(

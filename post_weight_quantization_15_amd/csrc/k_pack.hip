@@ -48,60 +48,69 @@ __global__ __launch_bounds__(256) void pack_kernel(
   qweight[r * words + w] = word;
 }
 
-// scales[r][g] = scalesP[g][r], zeros likewise.
+// scales[r][g] = scalesP[g][r], zeros likewise (0 for signed codes: their
+// zero point is implicit).
 __global__ __launch_bounds__(256) void meta_kernel(
     const float* __restrict__ scalesP, const uint8_t* __restrict__ zerosP,
-    int64_t m, int64_t ng, float* __restrict__ scales,
+    int64_t m, int64_t ng, int sgn, float* __restrict__ scales,
     uint8_t* __restrict__ zeros) {
   const int64_t e = int64_t(blockIdx.x) * 256 + threadIdx.x;
   if (e >= m * ng) return;
   const int64_t r = e / ng, g = e % ng;
   scales[e] = scalesP[g * m + r];
-  zeros[e] = zerosP[g * m + r];
+  zeros[e] = sgn ? 0 : zerosP[g * m + r];
 }
 
+// Group of original column c: its processing group (dynamic groups,
+// [derivation] 8.3 group_id[pi_j] = floor(j / g)), its own contiguous group
+// (static groups, floor(c / g)), or 0 (whole-row grid).
 __global__ void gidx_kernel(const int32_t* __restrict__ pinv, int64_t d,
-                            int64_t gsize, int32_t* __restrict__ g_idx) {
+                            int64_t gsize, int stat, int32_t* __restrict__ g_idx) {
   const int64_t c = int64_t(blockIdx.x) * blockDim.x + threadIdx.x;
-  if (c < d) g_idx[c] = gsize > 0 ? static_cast<int32_t>(pinv[c] / gsize) : 0;
+  if (c >= d) return;
+  g_idx[c] = gsize <= 0 ? 0 : static_cast<int32_t>((stat ? c : int64_t(pinv[c])) / gsize);
 }
 
-// w_hat[r][c] = Delta * (code - z) of the processing group holding column c.
+// w_hat[r][c] = Delta * (code - z) of the group holding column c; signed
+// codes (the low `bits` bits of c - z) are sign-extended, z = 0.
 __global__ __launch_bounds__(256) void w_hat_kernel(
     const uint8_t* __restrict__ codesO, const float* __restrict__ scales,
     const uint8_t* __restrict__ zeros, const int32_t* __restrict__ g_idx,
-    int64_t m, int64_t d, int64_t ng, float* __restrict__ w_hat) {
+    int64_t m, int64_t d, int64_t ng, int sgn, int bits,
+    float* __restrict__ w_hat) {
   const int64_t c = int64_t(blockIdx.x) * 256 + threadIdx.x;
   const int64_t r = blockIdx.y;
   if (c >= d) return;
   const int64_t g = g_idx[c];
   const float s = scales[r * ng + g];
-  const float z = static_cast<float>(zeros[r * ng + g]);
-  w_hat[r * d + c] = s * (static_cast<float>(codesO[r * d + c]) - z);
+  const int code = codesO[r * d + c];
+  const float v = sgn ? static_cast<float>(code >= (1 << (bits - 1)) ? code - (1 << bits) : code)
+                      : static_cast<float>(code) - static_cast<float>(zeros[r * ng + g]);
+  w_hat[r * d + c] = s * v;
 }
 
 unsigned cdiv(int64_t a, int64_t b) { return static_cast<unsigned>((a + b - 1) / b); }
 
 }  // namespace
 
-gptq_status launch_outputs(int64_t m, int64_t d, int bits, int gsize,
-                           const uint8_t* codesP, const float* scalesP,
-                           const uint8_t* zerosP, const int32_t* pinv,
-                           uint8_t* codesO, uint32_t* qweight, float* scales,
-                           uint8_t* zeros, int32_t* g_idx, float* w_hat,
-                           hipStream_t st) {
+gptq_status launch_outputs(int64_t m, int64_t d, int bits, int gsize, int sgn,
+                           int stat, const uint8_t* codesP,
+                           const float* scalesP, const uint8_t* zerosP,
+                           const int32_t* pinv, uint8_t* codesO,
+                           uint32_t* qweight, float* scales, uint8_t* zeros,
+                           int32_t* g_idx, float* w_hat, hipStream_t st) {
   const int64_t ng = gsize > 0 ? (d + gsize - 1) / gsize : 1;
   const int64_t words = (d * bits + 31) / 32;
   unpermute_codes_kernel<<<dim3(cdiv(m, 64), cdiv(d, 64)), 256, 0, st>>>(codesP, m, d, pinv, codesO);
   GPTQ_CHECK_LAUNCH();
   pack_kernel<<<dim3(cdiv(words, 256), static_cast<unsigned>(m)), 256, 0, st>>>(codesO, m, d, bits, words, qweight);
   GPTQ_CHECK_LAUNCH();
-  meta_kernel<<<cdiv(m * ng, 256), 256, 0, st>>>(scalesP, zerosP, m, ng, scales, zeros);
+  meta_kernel<<<cdiv(m * ng, 256), 256, 0, st>>>(scalesP, zerosP, m, ng, sgn, scales, zeros);
   GPTQ_CHECK_LAUNCH();
-  gidx_kernel<<<cdiv(d, 256), 256, 0, st>>>(pinv, d, gsize, g_idx);
+  gidx_kernel<<<cdiv(d, 256), 256, 0, st>>>(pinv, d, gsize, stat, g_idx);
   GPTQ_CHECK_LAUNCH();
   if (w_hat) {
-    w_hat_kernel<<<dim3(cdiv(d, 256), static_cast<unsigned>(m)), 256, 0, st>>>(codesO, scales, zeros, g_idx, m, d, ng, w_hat);
+    w_hat_kernel<<<dim3(cdiv(d, 256), static_cast<unsigned>(m)), 256, 0, st>>>(codesO, scales, zeros, g_idx, m, d, ng, sgn, bits, w_hat);
     GPTQ_CHECK_LAUNCH();
   }
   return GPTQ_OK;

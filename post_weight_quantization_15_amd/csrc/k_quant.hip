@@ -22,41 +22,30 @@
 // Lazy update: v_mfma_f32_16x16x4_f32 (exact fp32 products, fp32 sums).
 #include <algorithm>
 
-#include "common.h"
+#include "chain.h"
 
 namespace gptq {
 namespace {
 
-constexpr int kB = 128;        // largest block handled by one chain launch
-constexpr int kRowLanes = 16;  // lanes per output row (one DPP row)
-constexpr int kCols = kB / kRowLanes;   // block columns per lane
-constexpr int kChainRows = 16; // output rows per 256-thread workgroup
-constexpr int kTp = kChainRows + 1;     // LDS pitch of the row tiles
+using chain::kB;
+using chain::kCols;
+using chain::kRowLanes;
 
 __device__ inline float to_f32(float x) { return x; }
 __device__ inline float to_f32(uint16_t x) { return __uint_as_float(uint32_t(x) << 16); }
 
-// Min-max grid widened to contain 0 (so z represents 0 exactly); a flat
-// (all-zero) range becomes [-1, 1].  Delta = (hi - lo) / (2^b - 1),
-// z = round(-lo / Delta), all in IEEE fp32.
-__device__ inline void fit_grid(float lo, float hi, float maxq, float& scale,
-                                float& zero) {
-  if (hi == lo) {
-    lo = -1.0f;
-    hi = 1.0f;
-  }
-  scale = (hi - lo) / maxq;
-  zero = fminf(fmaxf(rintf(-lo / scale), 0.0f), maxq);
-}
-
-// Whole-row grid on the original weights: one wave per row.
+// Grids fitted once on the ORIGINAL weights: the whole-row grid (g = d,
+// [derivation] section 10) or the static groups (contiguous original
+// columns [G g, (G + 1) g), 8.3).  One wave per (row, group); scale / zero
+// land at [G][r].
 template <class T>
-__global__ __launch_bounds__(64) void fit_rows_kernel(
-    const T* __restrict__ W, int64_t d, int64_t ldw, float maxq,
-    float* __restrict__ scale, uint8_t* __restrict__ zero) {
-  const int64_t r = blockIdx.x;
+__global__ __launch_bounds__(64) void fit_groups_kernel(
+    const T* __restrict__ W, int64_t m, int64_t d, int64_t ldw, int64_t g,
+    float maxq, int sym, float* __restrict__ scale, uint8_t* __restrict__ zero) {
+  const int64_t r = blockIdx.x, G = blockIdx.y;
+  const int64_t c0 = G * g, c1 = min(c0 + g, d);
   float lo = 0.0f, hi = 0.0f;
-  for (int64_t c = threadIdx.x; c < d; c += 64) {
+  for (int64_t c = c0 + threadIdx.x; c < c1; c += 64) {
     const float x = to_f32(W[r * ldw + c]);
     lo = fminf(lo, x);
     hi = fmaxf(hi, x);
@@ -67,10 +56,21 @@ __global__ __launch_bounds__(64) void fit_rows_kernel(
   }
   if (threadIdx.x == 0) {
     float s, z;
-    fit_grid(lo, hi, maxq, s, z);
-    scale[r] = s;
-    zero[r] = static_cast<uint8_t>(z);
+    chain::fit_grid(lo, hi, maxq, sym != 0, s, z);
+    scale[G * m + r] = s;
+    zero[G * m + r] = static_cast<uint8_t>(z);
   }
+}
+
+// A grid given by the caller ([m, n_g] row-major) into the [n_g][m] layout.
+__global__ __launch_bounds__(256) void grid_in_kernel(
+    const float* __restrict__ s_in, const uint8_t* __restrict__ z_in, int64_t m,
+    int64_t ng, float* __restrict__ scale, uint8_t* __restrict__ zero) {
+  const int64_t e = int64_t(blockIdx.x) * 256 + threadIdx.x;
+  if (e >= m * ng) return;
+  const int64_t r = e / ng, G = e % ng;
+  scale[G * m + r] = s_in[e];
+  zero[G * m + r] = z_in[e];
 }
 
 __global__ void pinv_kernel(const int32_t* __restrict__ perm, int64_t d,
@@ -119,256 +119,6 @@ __global__ __launch_bounds__(256) void rl_kernel(const float* __restrict__ R,
     const int k = e / kB, q = (e / kCols) % kRowLanes, t = e % kCols;
     const int c = q + kRowLanes * t;
     RL[blk * kB * kB + e] = (k <= c && c < bw) ? R[(i + k) * d + i + c] : 0.0f;
-  }
-}
-
-__device__ inline float row_bcast(float x, int src) {
-  // DPP row_newbcast: lane src of every 16-lane row to the whole row
-  switch (src) {
-#define GPTQ_BC(L) case L: return __int_as_float(__builtin_amdgcn_update_dpp( \
-      0, __float_as_int(x), 0x150 + L, 0xF, 0xF, false));
-    GPTQ_BC(0) GPTQ_BC(1) GPTQ_BC(2) GPTQ_BC(3) GPTQ_BC(4) GPTQ_BC(5)
-    GPTQ_BC(6) GPTQ_BC(7) GPTQ_BC(8) GPTQ_BC(9) GPTQ_BC(10) GPTQ_BC(11)
-    GPTQ_BC(12) GPTQ_BC(13) GPTQ_BC(14) GPTQ_BC(15)
-#undef GPTQ_BC
-  }
-  return x;
-}
-
-// min / max over the 16 lanes of a row
-__device__ inline void row_minmax(float& lo, float& hi) {
-#pragma unroll
-  for (int o = 1; o < kRowLanes; o <<= 1) {
-    lo = fminf(lo, __shfl_xor(lo, o));
-    hi = fmaxf(hi, __shfl_xor(hi, o));
-  }
-}
-
-// One block [i0, i0 + bw) of the column loop for 16 output rows per
-// workgroup.  Thread (row rr = tid / 16, lane q = tid % 16) holds w[t] =
-// W_work[r0 + rr][i0 + q + 16 t].  For each column k (owner lane k % 16, slot
-// k / 16): every lane quantizes its slot-k/16 value, the owner's residual
-// eta = (w - q) / R_kk is broadcast over the row, and each lane applies
-// w[t] -= eta R[k][q + 16 t] for its later slots (R is upper triangular, so
-// slots at or before column k receive 0).  This is the in-block step of
-// the column loop ([derivation] eq. (42)); the block's R is read from LDS in
-// the RL lane order.
-// FS: a dynamic group can only start at block offsets that are multiples of
-// FS (0 = the whole-row grid, no refits).  A group that starts inside the
-// block ends inside it (checked on the host), so every fit sees fully
-// compensated columns; a group that starts at the block start and reaches
-// past it also reads its later columns from WT (compensated by every
-// earlier block).
-// VEC: 0 = scalar global accesses, 1 = 16-byte ones, 2 = 16-byte ones and
-// a full 128-column block.
-// The quotients w / Delta and rho / R_jj are products with fp32
-// reciprocals; they differ from the IEEE quotients by at most an ulp, which
-// can only matter within 1e-6 of a rounding boundary.
-template <int FS, int VEC>
-__global__ __launch_bounds__(256) void chain_kernel(
-    const float* __restrict__ WT, int64_t m, int64_t d, const float* __restrict__ RL,
-    int64_t i0, int bw_arg, int bi, float maxq, int64_t gsize,
-    float* __restrict__ scalesP, uint8_t* __restrict__ zerosP,
-    uint8_t* __restrict__ codesP, float* __restrict__ E,
-    const float* __restrict__ R, int64_t sb0, int kn, const float* __restrict__ Esb) {
-  const int bw = VEC == 2 ? kB : bw_arg;
-  __shared__ __attribute__((aligned(16))) float rl[kB * kB];
-  __shared__ float tile[kB][kTp];
-  __shared__ uint8_t ctile[kB][kChainRows];
-  const int tid = threadIdx.x;
-  const int rr = tid >> 4, q = tid & 15;
-  const int64_t r0 = int64_t(blockIdx.x) * kChainRows;
-  const int64_t r = r0 + rr;
-  const bool act = r < m;
-  const int64_t rs = act ? r : m - 1;
-  // stage RL of this block (contiguous 64 KiB) and the block's columns of the
-  // workgroup's rows (one 64-byte run per column)
-  {
-    const f32x4* src = reinterpret_cast<const f32x4*>(RL + (i0 / bi) * int64_t(kB) * kB);
-    f32x4* dst = reinterpret_cast<f32x4*>(rl);
-    f32x4 buf[kB * kB / 4 / 256];
-#pragma unroll
-    for (int u = 0; u < kB * kB / 4 / 256; ++u) buf[u] = src[tid + 256 * u];
-#pragma unroll
-    for (int u = 0; u < kB * kB / 4 / 256; ++u) dst[tid + 256 * u] = buf[u];
-  }
-  {
-    const int c = tid >> 1, h = tid & 1;
-    float v[8];
-    if (c < bw) {
-      const float* col = WT + (i0 + c) * m + r0 + 8 * h;
-      if (VEC && r0 + 8 * h + 8 <= m) {
-        const f32x4 a = *reinterpret_cast<const f32x4*>(col);
-        const f32x4 b = *reinterpret_cast<const f32x4*>(col + 4);
-        v[0] = a[0]; v[1] = a[1]; v[2] = a[2]; v[3] = a[3];
-        v[4] = b[0]; v[5] = b[1]; v[6] = b[2]; v[7] = b[3];
-      } else {
-#pragma unroll
-        for (int u = 0; u < 8; ++u) v[u] = (r0 + 8 * h + u < m) ? col[u] : 0.0f;
-      }
-    } else {
-#pragma unroll
-      for (int u = 0; u < 8; ++u) v[u] = 0.0f;
-    }
-#pragma unroll
-    for (int u = 0; u < 8; ++u) tile[c][8 * h + u] = v[u];
-  }
-  __syncthreads();
-  if (kn > 0) {
-    // the earlier blocks of this lazy batch, not yet applied to WT:
-    // tile[c][rr] -= sum_{k < kn} Esb[k][r0 + rr] R[sb0 + k][i0 + c]
-    // (wave wv: columns 32 wv .. 32 wv + 31 as two 16 x 16 MFMA blocks)
-    const int wv = tid >> 6, l = tid & 63, lr = l & 15, lk = l >> 4;
-    const float* Ea = Esb + min(r0 + lr, m - 1);
-    const float* Rb0 = R + sb0 * d + min(i0 + 32 * wv + lr, d - 1);
-    const float* Rb1 = R + sb0 * d + min(i0 + 32 * wv + 16 + lr, d - 1);
-    f32x4 acc0 = {0.f, 0.f, 0.f, 0.f}, acc1 = {0.f, 0.f, 0.f, 0.f};
-    // 32 k per batch (kn is a multiple of 32), the next batch's loads in
-    // flight during the current batch's products
-    float a[2][8], b0[2][8], b1[2][8];
-    auto fetch = [&](int buf, int k0) {
-#pragma unroll
-      for (int u = 0; u < 8; ++u) {
-        const int64_t k = k0 + 4 * u + lk;
-        a[buf][u] = Ea[k * m];
-        b0[buf][u] = Rb0[k * d];
-        b1[buf][u] = Rb1[k * d];
-      }
-    };
-    auto mma = [&](int buf) {
-#pragma unroll
-      for (int u = 0; u < 8; ++u) {
-        acc0 = __builtin_amdgcn_mfma_f32_16x16x4f32(a[buf][u], b0[buf][u], acc0, 0, 0, 0);
-        acc1 = __builtin_amdgcn_mfma_f32_16x16x4f32(a[buf][u], b1[buf][u], acc1, 0, 0, 0);
-      }
-    };
-    fetch(0, 0);
-    for (int k0 = 0; k0 < kn; k0 += 64) {
-      if (k0 + 32 < kn) fetch(1, k0 + 32);
-      mma(0);
-      if (k0 + 32 >= kn) break;
-      if (k0 + 64 < kn) fetch(0, k0 + 64);
-      mma(1);
-    }
-    // D[row 4 lk + v][column lr] of each block
-#pragma unroll
-    for (int v = 0; v < 4; ++v) {
-      tile[32 * wv + lr][4 * lk + v] -= acc0[v];
-      tile[32 * wv + 16 + lr][4 * lk + v] -= acc1[v];
-    }
-    __syncthreads();
-  }
-  float w[kCols], rinv[kCols], eta[kCols], code[kCols];
-#pragma unroll
-  for (int t = 0; t < kCols; ++t) {
-    const int c = q + kRowLanes * t;
-    w[t] = tile[c][rr];
-    const float rjj = rl[(c * kRowLanes + q) * kCols + t];
-    rinv[t] = c < bw ? 1.0f / rjj : 0.0f;
-    eta[t] = 0.0f;
-    code[t] = 0.0f;
-  }
-  // grid in force at the block start: the row grid, or the dynamic group
-  // that contains column i0 (fitted by this launch if it starts here, by an
-  // earlier launch otherwise)
-  const int64_t g0 = (FS == 0) ? 0 : i0 / gsize;
-  float scale = scalesP[g0 * m + rs];
-  float zero = static_cast<float>(zerosP[g0 * m + rs]);
-  float inv_scale = 1.0f / scale;
-  // R rows of the next kPf columns in registers (the LDS latency stays off
-  // the column-to-column dependence)
-  constexpr int kPf = 4;
-  f32x4 pa[kPf], pb[kPf];
-#pragma unroll
-  for (int p = 0; p < kPf; ++p) {
-    const float* rp = rl + (p * kRowLanes + q) * kCols;
-    pa[p] = *reinterpret_cast<const f32x4*>(rp);
-    pb[p] = *reinterpret_cast<const f32x4*>(rp + 4);
-  }
-#pragma clang loop unroll(full)
-  for (int tk = 0; tk < kCols; ++tk) {
-#pragma clang loop unroll(full)
-  for (int qk = 0; qk < kRowLanes; ++qk) {
-    const int k = kRowLanes * tk + qk;
-    // uniform: columns past a partial block (a full block has none, and
-    // its column steps are one straight run the compiler can pipeline)
-    if (VEC != 2 && k >= bw) continue;
-    if (FS > 0 && k % (FS > 0 ? FS : 1) == 0 && (i0 + k) % gsize == 0) {
-      const int64_t col = i0 + k;
-      const int64_t gend = min(col + gsize, d);
-      float lo = 0.0f, hi = 0.0f;
-#pragma unroll
-      for (int t = tk; t < kCols; ++t) {
-        const int64_t c = i0 + q + kRowLanes * t;
-        if (c >= col && c < gend && c < i0 + bw) {
-          lo = fminf(lo, w[t]);
-          hi = fmaxf(hi, w[t]);
-        }
-      }
-      for (int64_t cc = i0 + bw + q; cc < gend; cc += kRowLanes) {
-        const float x = WT[cc * m + rs];
-        lo = fminf(lo, x);
-        hi = fmaxf(hi, x);
-      }
-      row_minmax(lo, hi);
-      fit_grid(lo, hi, maxq, scale, zero);
-      inv_scale = 1.0f / scale;
-      if (q == 0 && act) {
-        scalesP[(col / gsize) * m + r] = scale;
-        zerosP[(col / gsize) * m + r] = static_cast<uint8_t>(zero);
-      }
-    }
-    // c - z = clamp(rint(x / scale), -z, maxq - z) (small integers, exact),
-    // and w - q = x - scale (c - z) in one rounding: six dependent
-    // operations from the column's value to its residual
-    const float x = w[tk];
-    const float cz = fminf(fmaxf(rintf(x * inv_scale), -zero), maxq - zero);
-    const float e = fmaf(-scale, cz, x) * rinv[tk];
-    if (q == qk) {
-      code[tk] = cz + zero;
-      eta[tk] = e;
-    }
-    const float eb = row_bcast(e, qk);
-    const int sl = k % kPf;
-    const f32x4 ra = pa[sl], rb = pb[sl];
-    // keep every element of this column's rows live up to here: a row
-    // register with a dead element could be reused while its load is in
-    // flight, which would make the next load wait
-    asm volatile("" :: "v"(ra), "v"(rb));
-    if (k + kPf < kB) {
-      const float* rp = rl + ((k + kPf) * kRowLanes + q) * kCols;
-      if (k + kPf < 4 * kRowLanes) pa[sl] = *reinterpret_cast<const f32x4*>(rp);
-      pb[sl] = *reinterpret_cast<const f32x4*>(rp + 4);
-    }
-    if (tk < 4) {
-#pragma unroll
-      for (int t = tk; t < 4; ++t) w[t] = fmaf(-eb, ra[t], w[t]);
-    }
-#pragma unroll
-    for (int t = (tk > 4 ? tk : 4); t < kCols; ++t) w[t] = fmaf(-eb, rb[t - 4], w[t]);
-  }
-  }
-  // codes and residuals out through LDS, one coalesced run per column
-  __syncthreads();
-#pragma unroll
-  for (int t = 0; t < kCols; ++t) {
-    const int cidx = q + kRowLanes * t;
-    tile[cidx][rr] = eta[t];
-    ctile[cidx][rr] = static_cast<uint8_t>(code[t]);
-  }
-  __syncthreads();
-  {
-    const int c = tid >> 1, h = tid & 1;
-    if (c < bw) {
-      float* erow = E + int64_t(c) * m + r0 + 8 * h;
-      uint8_t* crow = codesP + (i0 + c) * m + r0 + 8 * h;
-#pragma unroll
-      for (int u = 0; u < 8; ++u)
-        if (r0 + 8 * h + u < m) {
-          erow[u] = tile[c][8 * h + u];
-          crow[u] = ctile[c][8 * h + u];
-        }
-    }
   }
 }
 
@@ -488,16 +238,24 @@ unsigned cdiv(int64_t a, int64_t b) { return static_cast<unsigned>((a + b - 1) /
 
 }  // namespace
 
-gptq_status launch_fit_rows(const void* W, gptq_dtype dt, int64_t m, int64_t d,
-                            int64_t ldw, int bits, float* scale, uint8_t* zero,
-                            hipStream_t st) {
-  const float maxq = static_cast<float>((1 << bits) - 1);
+gptq_status launch_fit_grids(const void* W, gptq_dtype dt, int64_t m, int64_t d,
+                             int64_t ldw, int64_t g, float maxq, int sym,
+                             float* scalesP, uint8_t* zerosP, hipStream_t st) {
+  const dim3 grid(static_cast<unsigned>(m), cdiv(d, g));
   if (dt == GPTQ_F32)
-    fit_rows_kernel<float><<<static_cast<unsigned>(m), 64, 0, st>>>(
-        static_cast<const float*>(W), d, ldw, maxq, scale, zero);
+    fit_groups_kernel<float><<<grid, 64, 0, st>>>(
+        static_cast<const float*>(W), m, d, ldw, g, maxq, sym, scalesP, zerosP);
   else
-    fit_rows_kernel<uint16_t><<<static_cast<unsigned>(m), 64, 0, st>>>(
-        static_cast<const uint16_t*>(W), d, ldw, maxq, scale, zero);
+    fit_groups_kernel<uint16_t><<<grid, 64, 0, st>>>(
+        static_cast<const uint16_t*>(W), m, d, ldw, g, maxq, sym, scalesP, zerosP);
+  GPTQ_CHECK_LAUNCH();
+  return GPTQ_OK;
+}
+
+gptq_status launch_grid_in(const float* s_in, const uint8_t* z_in, int64_t m,
+                           int64_t ng, float* scalesP, uint8_t* zerosP,
+                           hipStream_t st) {
+  grid_in_kernel<<<cdiv(m * ng, 256), 256, 0, st>>>(s_in, z_in, m, ng, scalesP, zerosP);
   GPTQ_CHECK_LAUNCH();
   return GPTQ_OK;
 }
@@ -525,48 +283,15 @@ gptq_status launch_rbt(const float* R, int64_t d, int bi, float* RL,
   return GPTQ_OK;
 }
 
-gptq_status launch_chain(float* WT, int64_t m, int64_t d, const float* RL,
-                         int64_t i0, int bw, int bi, int bits, int64_t gsize,
-                         float* scalesP, uint8_t* zerosP, uint8_t* codesP,
-                         float* E, const float* R, int64_t sb0, const float* Esb,
-                         hipStream_t st) {
-  const int kn = static_cast<int>(i0 - sb0);
-  if (kn % 32 != 0) return GPTQ_ERR_INVALID_ARG;
-  const float maxq = static_cast<float>((1 << bits) - 1);
-  int fs = 0;
-  if (gsize > 0) {
-    fs = 1;
-    while (fs < kB && gsize % (2 * fs) == 0) fs *= 2;
-  }
-  const bool vec = m % 4 == 0 && reinterpret_cast<uintptr_t>(WT) % 16 == 0;
-  const dim3 grid(cdiv(m, kChainRows));
-#define GPTQ_CHAIN(FSV, V)                                                     \
-  chain_kernel<FSV, V><<<grid, 256, 0, st>>>(WT, m, d, RL, i0, bw, bi, maxq,  \
-                                             gsize, scalesP, zerosP, codesP, E, \
-                                             R, sb0, kn, Esb)
-#define GPTQ_CHAIN_FS(V)                     \
-  switch (fs) {                              \
-    case 0: GPTQ_CHAIN(0, V); break;         \
-    case 1: GPTQ_CHAIN(1, V); break;         \
-    case 2: GPTQ_CHAIN(2, V); break;         \
-    case 4: GPTQ_CHAIN(4, V); break;         \
-    case 8: GPTQ_CHAIN(8, V); break;         \
-    case 16: GPTQ_CHAIN(16, V); break;       \
-    case 32: GPTQ_CHAIN(32, V); break;       \
-    case 64: GPTQ_CHAIN(64, V); break;       \
-    default: GPTQ_CHAIN(128, V); break;      \
-  }
-  if (vec && bw == kB) {
-    GPTQ_CHAIN_FS(2)
-  } else if (vec) {
-    GPTQ_CHAIN_FS(1)
-  } else {
-    GPTQ_CHAIN_FS(0)
-  }
-#undef GPTQ_CHAIN_FS
-#undef GPTQ_CHAIN
-  GPTQ_CHECK_LAUNCH();
-  return GPTQ_OK;
+gptq_status launch_chain(const ChainArgs& a, hipStream_t st) {
+  if (a.kn % 32 != 0) return GPTQ_ERR_INVALID_ARG;
+  if (a.fs == chain::kFsStatic) return launch_chain_static(a, st);
+  if (a.fs == chain::kFsRow) return launch_chain_row(a, st);
+  // dynamic groups: the largest instantiated granularity that divides g
+  if (a.gsize % 128 == 0) return launch_chain_g128(a, st);
+  if (a.gsize % 64 == 0) return launch_chain_g64(a, st);
+  if (a.gsize % 8 == 0) return launch_chain_g8(a, st);
+  return launch_chain_g1(a, st);
 }
 
 gptq_status launch_lazy_update(float* WT, int64_t m, int64_t d, const float* R,

@@ -42,18 +42,29 @@ def test_status_strings(lib):
     assert lib.gptq_status_string(99) == b"unknown status"
 
 
-def params(bits=4, g=-1, b=128, damp=0.01, act=0):
-    return gq._Params(bits, g, b, damp, act)
+def params(bits=4, g=-1, b=128, damp=0.01, act=0, grid=0, static=0,
+           fs=None, fz=None):
+    return gq._Params(bits, g, b, damp, act, grid, static, fs, fz)
 
 
 @pytest.mark.parametrize("kw", [
     dict(bits=5), dict(bits=1), dict(g=0), dict(g=-2), dict(b=0),
     dict(damp=-0.1), dict(damp=float("nan")), dict(damp=float("inf")),
-    dict(act=2), dict(g=96, b=128),
+    dict(act=2), dict(g=96, b=128), dict(grid=3), dict(grid=-1), dict(static=2),
+    dict(grid=2), dict(grid=2, fs=0x1000), dict(grid=0, fs=0x1000, fz=0x1000),
+    dict(grid=1, fz=0x1000),
 ])
 def test_workspace_query_rejects_bad_params(lib, kw):
     p = params(**kw)
     assert lib.gptq_workspace_bytes(256, 512, ctypes.byref(p), 1) == 0
+
+
+def test_workspace_query_accepts_variants(lib):
+    ok = [params(4, 96, 128, static=1), params(2, 8, 128, grid=1),
+          params(3, 96, 128, grid=2, fs=0x1000, fz=0x1000),
+          params(4, -1, 128, grid=2, fs=0x1000, fz=0x1000), params(8, -1, 7, grid=1)]
+    for p in ok:
+        assert lib.gptq_workspace_bytes(256, 512, ctypes.byref(p), 1) > 0
 
 
 def test_workspace_query_sizes(lib):
@@ -133,3 +144,82 @@ def test_binding_refuses_host_tensors():
     X = torch.zeros(3, 4, dtype=torch.bfloat16)
     with pytest.raises(ValueError):
         gq.gptq_hessian_accumulate(S, X)
+
+
+def test_binding_rejects_overlapping_rows_and_wrong_types():
+    """Checks done before any device pointer is taken (CPU tensors)."""
+    import torch
+    S = torch.zeros(8, 8)
+    X = torch.zeros(1, 8).expand(5, 8)          # stride (0, 1): rows overlap
+    with pytest.raises(ValueError, match="overlap"):
+        gq.gptq_hessian_accumulate(S, X)
+    with pytest.raises(TypeError):
+        gq.gptq_hessian_accumulate(S.double(), torch.zeros(5, 8))
+    W = torch.zeros(1, 8).expand(4, 8)
+    with pytest.raises(ValueError, match="overlap"):
+        gq.gptq_quantize_layer(W, S, 5)
+    W = torch.zeros(4, 8)
+    with pytest.raises(TypeError, match="perm"):
+        gq.gptq_quantize_layer(W, None, 0, R=torch.zeros(8, 8),
+                               perm=torch.zeros(8, dtype=torch.int64),
+                               dead=torch.zeros(8, dtype=torch.uint8))
+    with pytest.raises(TypeError, match="R"):
+        gq.gptq_quantize_layer(W, None, 0, R=torch.zeros(8, 8, dtype=torch.float64),
+                               perm=torch.zeros(8, dtype=torch.int32),
+                               dead=torch.zeros(8, dtype=torch.uint8))
+    with pytest.raises(ValueError, match="together"):
+        gq.gptq_quantize_layer(W, S, 5, R=torch.zeros(8, 8))
+    with pytest.raises(ValueError):
+        gq.gptq_cholesky_inverse(torch.zeros(8, 7), 5)
+    with pytest.raises(ValueError, match="contiguous"):
+        gq.gptq_cholesky_inverse(torch.zeros(8, 8).T, 5)
+    with pytest.raises(TypeError):
+        gq.gptq_cholesky_inverse(torch.zeros(8, 8, dtype=torch.float64), 5)
+
+
+def test_dequant_matmul_rejects(lib):
+    INV = gq.GPTQ_ERR_INVALID_ARG
+    f = lib.gptq_dequant_matmul
+    ok = dict(X=FAKE, dt=0, n=4, d=64, ldx=64, qw=FAKE, sc=FAKE, zp=FAKE, gi=FAKE,
+              m=32, bits=4, g=32, sgn=0, Y=FAKE, ldy=32)
+
+    def call(**kw):
+        a = dict(ok, **kw)
+        return f(a["X"], a["dt"], a["n"], a["d"], a["ldx"], a["qw"], a["sc"], a["zp"],
+                 a["gi"], a["m"], a["bits"], a["g"], a["sgn"], a["Y"], a["ldy"], None)
+
+    for kw in (dict(dt=1), dict(n=-1), dict(d=0), dict(m=0), dict(ldx=63), dict(ldy=31),
+               dict(bits=5), dict(g=0), dict(g=-2), dict(sgn=2), dict(X=None),
+               dict(qw=None), dict(sc=None), dict(zp=None), dict(gi=None), dict(Y=None),
+               dict(d=70000, ldx=70000)):
+        assert call(**kw) == INV, kw
+    # n = 0 launches nothing and succeeds without a GPU
+    assert call(n=0, X=None, Y=None) == gq.GPTQ_OK
+
+
+def test_stack_rejects(lib):
+    """Descriptor validation of the layer-by-layer driver (no GPU work)."""
+    INV = gq.GPTQ_ERR_INVALID_ARG
+    F = 0x1000
+
+    def layer(m, d, **kw):
+        p = params(**kw)
+        return gq._StackLayer(F, 0, m, d, d, p, F, F, F, F)
+
+    two = (gq._StackLayer * 2)(layer(64, 128), layer(32, 64))
+    assert lib.gptq_stack_workspace_bytes(two, 2, 1000) > 0
+    bad_dims = (gq._StackLayer * 2)(layer(64, 128), layer(32, 65))
+    assert lib.gptq_quantize_stack(bad_dims, 2, FAKE, 1000, 0, FAKE, None, FAKE,
+                                   1 << 40, None) == INV
+    assert lib.gptq_quantize_stack(two, 2, FAKE, 1000, 3, FAKE, None, FAKE, 1 << 40,
+                                   None) == INV
+    assert lib.gptq_quantize_stack(two, 2, None, 1000, 0, FAKE, None, FAKE, 1 << 40,
+                                   None) == INV
+    assert lib.gptq_quantize_stack(two, 2, FAKE, 0, 0, FAKE, None, FAKE, 1 << 40,
+                                   None) == INV
+    assert lib.gptq_quantize_stack(two, 0, FAKE, 10, 0, FAKE, None, FAKE, 1 << 40,
+                                   None) == INV
+    badp = (gq._StackLayer * 1)(layer(64, 128, bits=5))
+    assert lib.gptq_stack_workspace_bytes(badp, 1, 1000) == 0
+    assert lib.gptq_quantize_stack(two, 2, FAKE, 1000, 0, FAKE, None, FAKE, 16,
+                                   None) == gq.GPTQ_ERR_WORKSPACE

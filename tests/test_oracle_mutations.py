@@ -90,6 +90,17 @@ MUTATIONS = {
     # static group ids permuted like dynamic ones
     "static_gidx_permuted": ("        g_idx = np.arange(d) // group_size\n",
                              "        g_idx[perm] = np.arange(d) // group_size\n"),
+    # dequantization ignoring the group id of each column
+    "dequant_no_gidx": ("return scales[rows, g_idx[None, :]] * (codes - zeros[rows, g_idx[None, :]])",
+                        "return scales[rows, :1] * (codes - zeros[rows, :1])"),
+    # signed codes not sign-extended
+    "dequant_no_sign": ("codes = np.where(codes >= 2 ** (bits - 1), codes - 2 ** bits, codes)",
+                        "pass"),
+    # next layer fed by the unquantized layer's outputs
+    "stack_float_propagation": ("Y = dequant_matmul(X, res.packed, res.scales, zeros, res.g_idx,",
+                                "Y = X @ W.T if True else dequant_matmul(X, res.packed, res.scales, zeros, res.g_idx,"),
+    # activation skipped between layers
+    "stack_no_activation": ("X = bf16_round(activate(Y, activation))", "X = bf16_round(Y)"),
     # symmetric codes stored unsigned
     "signed_codes_unsigned": ("return np.mod(res.codes - z, 2 ** bits)",
                               "return res.codes"),

@@ -187,3 +187,20 @@ def test_zero_point_rounds_to_nearest():
     c, q, _ = orc.encode(np.array([0.0, -1.15, 1.85]), sc[0], z[0], 4)
     assert q[0] == 0.0
     assert abs(q[1] + 1.15) <= 0.1 + 1e-7 and abs(q[2] - 1.85) <= 0.1 + 1e-7
+
+
+def test_sixteen_level_example_dequant_matmul():
+    """[derivation] section 11: the stored codes K with Delta = 0.25, z = 8
+    dequantize to the page's W_hat, and the quantized layer's outputs are
+    the page's Y plus its printed Y_hat - Y."""
+    g = load_golden("sixteen_level_example.json")
+    K = np.array(g["K"])
+    packed = orc.pack_codes(K, 4)
+    sc = np.full((2, 1), g["scale"])
+    z = np.full((2, 1), g["zero"])
+    gi = np.zeros(2, dtype=np.int64)
+    np.testing.assert_allclose(orc.dequantize(packed, sc, z, gi, 2, 4), g["W_hat"],
+                               atol=1e-15)
+    Y_hat = orc.dequant_matmul(np.array(g["A0"]), packed, sc, z, gi, 4)
+    np.testing.assert_allclose(Y_hat.T, np.array(g["Y"]) + np.array(g["Yhat_minus_Y"]),
+                               atol=1e-12)

@@ -522,3 +522,56 @@ def test_static_groups_any_blocksize():
                            static_groups=True, act_order=True) for b in (1, 7, 128)]
     for o in outs[1:]:
         np.testing.assert_array_equal(o.codes, outs[0].codes)
+
+
+@pytest.mark.parametrize("group_size,act_order", [(-1, False), (8, True)])
+def test_dequantize_stored_format_equals_loop_values(group_size, act_order):
+    """Dequantizing the stored format (packed codes, scales, zeros, group
+    ids) gives back the values the column loop quantized to -- for dynamic
+    groups under act-order, static groups and the signed symmetric grid."""
+    rng = np.random.default_rng(17)
+    W, Xt = rand_layer(rng, 9, 40, 150)
+    Xt[:, 11] *= 7.0
+    S = orc.hessian_sum(Xt)
+    for kw in (dict(), dict(static_groups=True), dict(symmetric=True)):
+        res = orc.gptq_layer(W, S, 150, bits=3, group_size=group_size, blocksize=8,
+                             act_order=act_order, **kw)
+        zeros = np.zeros_like(res.zeros) if res.signed else res.zeros
+        Wd = orc.dequantize(res.packed, res.scales, zeros, res.g_idx, 40, 3,
+                            signed=res.signed)
+        np.testing.assert_allclose(Wd, res.w_hat, atol=1e-15)
+        x = rng.standard_normal((5, 40))
+        np.testing.assert_allclose(
+            orc.dequant_matmul(x, res.packed, res.scales, zeros, res.g_idx, 3,
+                               signed=res.signed), x @ res.w_hat.T, atol=1e-12)
+
+
+def test_bf16_round_against_torch():
+    """bf16_round agrees with torch's float32 -> bfloat16 conversion (round
+    to nearest even) on values exactly representable in float32."""
+    import torch
+    rng = np.random.default_rng(23)
+    v = np.concatenate([rng.standard_normal(5000) * 10 ** rng.uniform(-6, 6, 5000),
+                        [1.0 + 2.0 ** -8, 1.0 + 3 * 2.0 ** -8, -2.5, 0.0, 255.5]])
+    v32 = v.astype(np.float32)
+    ref = torch.from_numpy(v32).to(torch.bfloat16).to(torch.float64).numpy()
+    np.testing.assert_array_equal(orc.bf16_round(v32.astype(np.float64)), ref)
+
+
+def test_stack_layer_inputs_are_previous_outputs():
+    """Layer-wise quantization: layer l+1's statistics come from layer l's
+    quantized outputs; the first layer equals a lone gptq_layer call."""
+    rng = np.random.default_rng(29)
+    X0 = np.round(rng.standard_normal((300, 24)) * 2) / 2
+    Ws = [0.05 * rng.standard_normal((16, 24)), 0.05 * rng.standard_normal((12, 16))]
+    ps = [dict(bits=4, group_size=8, blocksize=8), dict(bits=3, group_size=-1, blocksize=4)]
+    out, Xf = orc.gptq_stack(Ws, X0, ps, activation="relu")
+    lone = orc.gptq_layer(Ws[0], orc.hessian_sum(X0), 300, **ps[0])
+    np.testing.assert_array_equal(out[0]["res"].codes, lone.codes)
+    X1 = orc.bf16_round(np.maximum(X0 @ lone.w_hat.T, 0.0))
+    np.testing.assert_array_equal(out[1]["X"], X1)
+    np.testing.assert_allclose(out[1]["S"], X1.T @ X1, rtol=1e-12)
+    direct = np.sum(((Ws[1] - out[1]["res"].w_hat) @ X1.T) ** 2) / 300
+    assert abs(out[1]["err"] - direct) <= 1e-12 * direct
+    np.testing.assert_array_equal(
+        Xf, orc.bf16_round(np.maximum(X1 @ out[1]["res"].w_hat.T, 0.0)))
