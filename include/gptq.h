@@ -19,7 +19,9 @@
  *     keeps between calls, per device, until the process ends: one internal
  *     non-blocking stream and two events (created, under a mutex, by the
  *     first factorisation on that device, with the caller stream's device
- *     current).  Calls that share a workspace must not overlap.
+ *     current); a library-owned static scratch array and its address (see
+ *     gptq_hessian_accumulate_noalloc).  Calls that share a workspace must
+ *     not overlap.
  *   - Sizes: every matrix dimension (d, and m for the quantizer) is at most
  *     65535 (one grid dimension per row/column in several launches); larger
  *     values are rejected with GPTQ_ERR_INVALID_ARG.
@@ -125,6 +127,26 @@ gptq_status gptq_hessian_accumulate(float* S, int64_t d, const void* X,
                                     gptq_dtype x_dtype, int64_t n_tok,
                                     int64_t ldx, void* ws, size_t ws_bytes,
                                     void* stream);
+
+/* ---------------------------------------------------------------------------
+ * Allocation-free variant of gptq_hessian_accumulate, for callers that cannot
+ * allocate device memory (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid allocation).  Same operation, arguments and errors,
+ * without ws: the token-split partial sums live in a static device array of
+ * GPTQ_NOALLOC_SCRATCH_BYTES that the library owns (one per GPU it runs on,
+ * held until the process ends).  The split plan is chosen to fit that array,
+ * so larger problems run with fewer (longer) token splits than
+ * gptq_hessian_accumulate may use: S agrees with it to fp32 summation
+ * rounding, bit for bit when both plans coincide.  Every partial the call
+ * reads it has written itself, so no clearing is needed between calls.  The
+ * array is shared by every call on one GPU: calls that overlap on one GPU
+ * (other streams, other host threads) race on it and must be serialised by
+ * the caller.  Calls no hipMalloc/hipFree.
+ * ------------------------------------------------------------------------- */
+#define GPTQ_NOALLOC_SCRATCH_BYTES ((size_t)256 << 20)
+gptq_status gptq_hessian_accumulate_noalloc(float* S, int64_t d, const void* X,
+                                            gptq_dtype x_dtype, int64_t n_tok,
+                                            int64_t ldx, void* stream);
 
 /* ---------------------------------------------------------------------------
  * Factor ([derivation] section 10 steps 5-6, eq. (37)-(40)).

@@ -18,19 +18,21 @@ __all__ = [
     "GPTQError", "lib_path", "load_library", "gptq_hessian_accumulate",
     "gptq_cholesky_inverse", "gptq_quantize_layer", "gptq_workspace_bytes",
     "gptq_hessian_workspace_bytes", "gptq_factor_workspace_bytes",
-    "gptq_dequant_matmul", "gptq_quantize_stack",
+    "gptq_hessian_accumulate_noalloc", "gptq_dequant_matmul", "gptq_quantize_stack",
     "EXPORTED_SYMBOLS", "GRIDS", "ACTIVATIONS", "GPTQ_OK", "GPTQ_ERR_INVALID_ARG", "GPTQ_ERR_NOT_SPD",
     "GPTQ_ERR_WORKSPACE", "GPTQ_ERR_HIP",
 ]
 
 GPTQ_OK, GPTQ_ERR_INVALID_ARG, GPTQ_ERR_NOT_SPD, GPTQ_ERR_WORKSPACE, GPTQ_ERR_HIP = range(5)
 GPTQ_BF16, GPTQ_F32 = 0, 1
+GPTQ_NOALLOC_SCRATCH_BYTES = 256 << 20      # include/gptq.h
 
 EXPORTED_SYMBOLS = (
     "gptq_status_string", "gptq_hessian_workspace_bytes",
     "gptq_hessian_accumulate", "gptq_factor_workspace_bytes",
     "gptq_cholesky_inverse", "gptq_workspace_bytes", "gptq_quantize_layer",
-    "gptq_dequant_matmul", "gptq_stack_workspace_bytes", "gptq_quantize_stack",
+    "gptq_hessian_accumulate_noalloc", "gptq_dequant_matmul",
+    "gptq_stack_workspace_bytes", "gptq_quantize_stack",
 )
 ACTIVATIONS = {"none": 0, "relu": 1, "silu": 2}
 
@@ -86,6 +88,8 @@ def load_library():
     lib.gptq_hessian_workspace_bytes.argtypes = [i64, i64]
     lib.gptq_hessian_accumulate.restype = ctypes.c_int
     lib.gptq_hessian_accumulate.argtypes = [vp, i64, vp, ctypes.c_int, i64, i64, vp, sz, vp]
+    lib.gptq_hessian_accumulate_noalloc.restype = ctypes.c_int
+    lib.gptq_hessian_accumulate_noalloc.argtypes = [vp, i64, vp, ctypes.c_int, i64, i64, vp]
     lib.gptq_dequant_matmul.restype = ctypes.c_int
     lib.gptq_dequant_matmul.argtypes = [vp, ctypes.c_int, i64, i64, i64, vp, vp, vp, vp,
                                         i64, i32, i32, i32, vp, i64, vp]
@@ -215,6 +219,25 @@ def gptq_hessian_accumulate(S: torch.Tensor, X: torch.Tensor, ws=None) -> torch.
                                      n_tok, ldx, _dev_ptr(ws),
                                      ws.numel(), _stream(S.device))
     _check(st, "gptq_hessian_accumulate")
+    return S
+
+
+def gptq_hessian_accumulate_noalloc(S: torch.Tensor, X: torch.Tensor) -> torch.Tensor:
+    """As gptq_hessian_accumulate, with the library's static scratch instead
+    of a workspace (no device allocation anywhere in the call)."""
+    if S.dim() != 2 or S.shape[0] != S.shape[1]:
+        raise ValueError("S must be a [d, d] tensor")
+    d = S.shape[0]
+    _expect(S, "S", torch.float32, (d, d), S.device)
+    if X.dim() != 2 or X.shape[1] != d:
+        raise ValueError("X must be [n_tok, d]")
+    if X.device != S.device:
+        raise ValueError("X and S must be on the same device")
+    ldx = _row_stride(X, "X")
+    dtc = _dtype_code(X)
+    st = _lib().gptq_hessian_accumulate_noalloc(_dev_ptr(S), d, _dev_ptr(X), dtc,
+                                                X.shape[0], ldx, _stream(S.device))
+    _check(st, "gptq_hessian_accumulate_noalloc")
     return S
 
 

@@ -2,11 +2,49 @@
 // launch sequencing on the caller's stream and the damping retry.
 #include <algorithm>
 #include <cmath>
+#include <mutex>
 
 #include "common.h"
 
 namespace gptq {
 namespace {
+
+// Scratch of the allocation-free Hessian entry point: the split partial
+// tiles.  Every GPU the library runs on holds its own copy until the process
+// ends.  In host code `scratch` names a host-side stand-in, not the device
+// array: its device address is looked up once per device (with that device
+// current) and only that address is passed to kernels.
+constexpr size_t kScratchBytes = GPTQ_NOALLOC_SCRATCH_BYTES;
+__device__ __align__(256) unsigned char scratch[kScratchBytes];
+
+constexpr int kMaxScratchDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxScratchDevices] = {};
+
+// Device address of `scratch` on the device that runs `st` (the current
+// device for the null stream).
+gptq_status scratch_address(hipStream_t st, void** out) {
+  *out = nullptr;
+  int dev = 0;
+  if (st)
+    GPTQ_CHECK_HIP(hipStreamGetDevice(st, &dev));
+  else
+    GPTQ_CHECK_HIP(hipGetDevice(&dev));
+  if (dev < 0 || dev >= kMaxScratchDevices) return GPTQ_ERR_HIP;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    int cur = 0;
+    GPTQ_CHECK_HIP(hipGetDevice(&cur));
+    if (cur != dev) GPTQ_CHECK_HIP(hipSetDevice(dev));
+    void* p = nullptr;
+    const hipError_t e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (cur != dev) GPTQ_CHECK_HIP(hipSetDevice(cur));
+    if (e != hipSuccess || !p) return GPTQ_ERR_HIP;
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return GPTQ_OK;
+}
 
 constexpr int64_t kMaxDim = 65535;   // grid.y limit of the per-row launches
 constexpr int kChainMaxBlock = 128;
@@ -307,6 +345,23 @@ gptq_status gptq_hessian_accumulate(float* S, int64_t d, const void* X,
   if (ws_bytes < need || (need > 0 && !ws)) return GPTQ_ERR_WORKSPACE;
   return launch_hessian(S, d, X, x_dtype, n_tok, ldx, ws,
                         static_cast<hipStream_t>(stream));
+}
+
+gptq_status gptq_hessian_accumulate_noalloc(float* S, int64_t d, const void* X,
+                                            gptq_dtype x_dtype, int64_t n_tok,
+                                            int64_t ldx, void* stream) {
+  if (!S || d <= 0 || d > kMaxDim || n_tok < 0 || ldx < d || !valid_dtype(x_dtype))
+    return GPTQ_ERR_INVALID_ARG;
+  if (n_tok > 0 && !X) return GPTQ_ERR_INVALID_ARG;
+  const double cap = static_cast<double>(kScratchBytes);
+  // the token split is planned within the scratch size, so no size needs
+  // more; the check guards the plan itself
+  if (hessian_ws_bytes(d, n_tok, cap) > kScratchBytes) return GPTQ_ERR_WORKSPACE;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  void* ws = nullptr;
+  gptq_status s;
+  if ((s = scratch_address(st, &ws)) != GPTQ_OK) return s;
+  return launch_hessian(S, d, X, x_dtype, n_tok, ldx, ws, st, cap);
 }
 
 gptq_status gptq_dequant_matmul(const void* X, gptq_dtype x_dtype, int64_t n,

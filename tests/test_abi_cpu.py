@@ -146,6 +146,18 @@ def test_binding_refuses_host_tensors():
         gq.gptq_hessian_accumulate(S, X)
 
 
+def test_noalloc_hessian_rejects(lib):
+    INV = gq.GPTQ_ERR_INVALID_ARG
+    f = lib.gptq_hessian_accumulate_noalloc
+    assert f(None, 16, FAKE, 0, 4, 16, None) == INV
+    assert f(FAKE, 0, FAKE, 0, 4, 16, None) == INV
+    assert f(FAKE, 16, FAKE, 0, -1, 16, None) == INV
+    assert f(FAKE, 16, FAKE, 0, 4, 8, None) == INV
+    assert f(FAKE, 16, FAKE, 7, 4, 16, None) == INV
+    assert f(FAKE, 16, None, 0, 4, 16, None) == INV
+    assert f(FAKE, 70000, FAKE, 0, 4, 70000, None) == INV
+
+
 def test_binding_rejects_overlapping_rows_and_wrong_types():
     """Checks done before any device pointer is taken (CPU tensors)."""
     import torch
@@ -153,6 +165,8 @@ def test_binding_rejects_overlapping_rows_and_wrong_types():
     X = torch.zeros(1, 8).expand(5, 8)          # stride (0, 1): rows overlap
     with pytest.raises(ValueError, match="overlap"):
         gq.gptq_hessian_accumulate(S, X)
+    with pytest.raises(ValueError, match="overlap"):
+        gq.gptq_hessian_accumulate_noalloc(S, X)
     with pytest.raises(TypeError):
         gq.gptq_hessian_accumulate(S.double(), torch.zeros(5, 8))
     W = torch.zeros(1, 8).expand(4, 8)
