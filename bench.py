@@ -1,18 +1,22 @@
-"""Benchmark: one GPTQ linear layer end to end on one MI355X.
+"""Benchmark: GPTQ linear layers end to end on one MI355X.
 
-Workload: the attention-projection layer -- W 4096 x 4096 bf16 ~ N(0, 0.02),
-262144 calibration tokens (128 x 2048) of low-rank + noise activations with
-1% outlier channels x20, 4-bit, group 128, block 128, percdamp 0.01.
-Synthetic, seeded; inputs are resident in HBM before timing starts.
+Headline workload: the attention-projection layer -- W 4096 x 4096 bf16
+~ N(0, 0.02), 262144 calibration tokens (128 x 2048) of low-rank + noise
+activations with 1% outlier channels x20, 4-bit, group 128, block 128,
+percdamp 0.01.  Synthetic, seeded; inputs are resident in HBM before timing
+starts.
 
 One step = the whole hot path: zero S, S += X^T X over all tokens, then
 quantize the layer (H, dead fix, damping, R = chol(H^-1) upper, column loop
 with lazy block updates, unpermute + pack), outputs in HBM.
 
-Prints one JSON line.  The `roofline` object covers the dominant kernel,
-timed live with HIP events on the stream the library launches on; the
-`cpu_baseline` object is the float64 oracle timed on a bounded sample of the
-same layer on the host cores.
+Prints one JSON line.  `roofline` covers the dominant kernel (the statistics
+call), timed live with HIP events on the stream the library launches on;
+`phase_rooflines` covers the factorisation, the column chain and the lazy
+update, from the library's own per-phase event tracing over extra steps;
+`workloads` times the other layer shapes of the pages' workloads (one
+line each, inputs resident); `cpu_baseline` is the float64 oracle on a
+bounded sample of the headline layer on the host cores.
 """
 
 from __future__ import annotations
@@ -21,6 +25,7 @@ import argparse
 import hashlib
 import json
 import os
+import platform
 import sys
 import time
 
@@ -28,6 +33,8 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 PEAK_BF16_TFLOPS = 2500.0       # MI355X dense bf16 MFMA
+PEAK_FP32_TFLOPS = 157.3        # MI355X fp32 (matrix)
+PEAK_FP64_TFLOPS = 78.6         # MI355X fp64
 PEAK_HBM_GBS = 8000.0
 
 METRIC = "seconds per linear layer (4096x4096, 262144 tok, 4-bit g128); % MFMA/HBM peak"
@@ -44,6 +51,9 @@ def parse():
                     help="token sample for the oracle's statistics")
     ap.add_argument("--cpu-rows", type=int, default=256,
                     help="row sample for the oracle's column loop")
+    ap.add_argument("--workloads", default="all",
+                    help="comma list of extra workloads to time (tiny, mlp_up, mlp_down, "
+                         "large_attn, large_fc1, large_fc2, block), 'all' or 'none'")
     ap.add_argument("--phase", choices=("layer", "hessian"), default="layer",
                     help="'hessian' times only the statistics call (for counter passes)")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
@@ -57,9 +67,9 @@ def kernel_source_hash(name):
         return hashlib.sha256(f.read()).hexdigest()[:16]
 
 
-def traffic_from_profile(src_hash, launches_per_step=1):
-    """HBM bytes per launch of the Hessian kernel from the committed counter
-    summary, if it was taken on the current kernel source."""
+def traffic_from_profile(src_hash):
+    """HBM bytes per launch of the statistics kernels from the committed
+    counter summary, if it was taken on the current kernel source."""
     path = os.path.join(ROOT, "profiles", "hessian_attn_proj_traffic.json")
     try:
         with open(path) as f:
@@ -71,20 +81,45 @@ def traffic_from_profile(src_hash, launches_per_step=1):
     return rec.get("hbm_bytes_per_launch")
 
 
+def tensor_sha(t):
+    import torch
+    b = t.detach().contiguous().view(torch.uint8) if t.dtype != torch.uint8 else t
+    return hashlib.sha256(b.cpu().numpy().tobytes()).hexdigest()
+
+
+def host_info():
+    import numpy
+    import scipy
+    info = {"affinity_cores": len(os.sched_getaffinity(0)),
+            "numpy": numpy.__version__, "scipy": scipy.__version__,
+            "python": platform.python_version()}
+    try:
+        from threadpoolctl import threadpool_info
+        info["blas"] = [{k: p.get(k) for k in ("internal_api", "num_threads", "version")}
+                        for p in threadpool_info()]
+    except Exception:       # noqa: BLE001
+        info["blas"] = None
+    try:
+        with open("/proc/meminfo") as f:
+            kb = int(f.readline().split()[1])
+        info["host_ram_gib"] = round(kb / 2 ** 20, 1)
+    except OSError:
+        info["host_ram_gib"] = None
+    return info
+
+
 def cpu_baseline(W, X, params, n_tokens, cpu_tokens, cpu_rows):
     """The oracle as it stands, on a bounded sample, scaled to one layer."""
     import numpy as np
     import oracle as orc
-    try:
-        from threadpoolctl import threadpool_info
-        cores = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
-    except Exception:       # noqa: BLE001
-        cores = os.cpu_count()
+    info = host_info()
+    threads = [b.get("num_threads") or 1 for b in (info.get("blas") or [])] or [1]
     m, d = W.shape
     Xs = X[:cpu_tokens].float().cpu().numpy()
     t0 = time.perf_counter()
     S_part = orc.hessian_sum(Xs)
-    t_stats = (time.perf_counter() - t0) * (n_tokens / Xs.shape[0])
+    t_stats_s = time.perf_counter() - t0
+    t_stats = t_stats_s * (n_tokens / Xs.shape[0])
     S = S_part * (n_tokens / Xs.shape[0])       # stand-in statistics for timing
     t0 = time.perf_counter()
     H, perm, dead, damp = orc.prepare(S, n_tokens, params["percdamp"], params["act_order"])
@@ -101,13 +136,146 @@ def cpu_baseline(W, X, params, n_tokens, cpu_tokens, cpu_rows):
     codes = np.empty_like(out["codes"])
     codes[:, perm] = out["codes"]
     orc.pack_codes(codes, params["bits"])
-    t_loop = (time.perf_counter() - t0) * (m / Wr.shape[0])
+    t_loop_s = time.perf_counter() - t0
+    t_loop = t_loop_s * (m / Wr.shape[0])
     total = t_stats + t_factor + t_loop
-    return {"value": total, "unit": "s per layer", "cores": int(cores), "kind": "oracle",
-            "sample": (f"statistics on {Xs.shape[0]} of {n_tokens} tokens x{n_tokens / Xs.shape[0]:g}; "
-                       f"factor at full d={d}; column loop + packing on {Wr.shape[0]} of {m} rows "
-                       f"x{m / Wr.shape[0]:g}; phases s: stats {t_stats:.2f}, factor {t_factor:.2f}, "
-                       f"loop {t_loop:.2f}")}
+    return {"value": round(total, 3), "unit": "s per layer (extrapolated)",
+            "cores": int(max(threads)), "kind": "oracle",
+            "sample": (f"extrapolated: statistics measured on {Xs.shape[0]} of {n_tokens} tokens "
+                       f"({t_stats_s:.2f} s) x{n_tokens / Xs.shape[0]:g}; factor at full d={d} "
+                       f"({t_factor:.2f} s, measured); column loop + packing on {Wr.shape[0]} of {m} "
+                       f"rows ({t_loop_s:.2f} s) x{m / Wr.shape[0]:g}"),
+            "phases_s": {"stats": round(t_stats, 2), "factor": round(t_factor, 2),
+                         "loop": round(t_loop, 2)},
+            "host": info}
+
+
+def time_layer(gq, torch, W, X, params, steps, warmup, shared=None):
+    """Whole-path time of one layer (statistics + quantize), inputs resident."""
+    dev = W.device
+    m, d = W.shape
+    N = X.shape[0]
+    S = torch.zeros(d, d, dtype=torch.float32, device=dev)
+    hws = torch.empty(max(gq.gptq_hessian_workspace_bytes(d, N), 1), dtype=torch.uint8, device=dev)
+    qws = torch.empty(gq.gptq_workspace_bytes(m, d, **params), dtype=torch.uint8, device=dev)
+
+    def step():
+        S.zero_()
+        gq.gptq_hessian_accumulate(S, X, ws=hws)
+        return gq.gptq_quantize_layer(W, S, N, ws=qws, **params)
+
+    for _ in range(warmup):
+        step()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        step()
+    torch.cuda.synchronize()
+    return (time.perf_counter() - t0) / steps
+
+
+def time_block(gq, torch, B, steps, warmup):
+    """The decoder block's seven linears in order; q/k/v share one factor,
+    gate/up another."""
+    dev = B["q"]["W"].device
+    p = B["q"]["params"]
+
+    def stats(X):
+        d = X.shape[1]
+        S = torch.zeros(d, d, dtype=torch.float32, device=dev)
+        gq.gptq_hessian_accumulate(S, X)
+        return S
+
+    def step():
+        for names in (("q", "k", "v"), ("o",), ("gate", "up"), ("down",)):
+            X = B[names[0]]["X"]
+            S = stats(X)
+            if len(names) > 1:
+                R, perm, dead, _ = gq.gptq_cholesky_inverse(S, X.shape[0], p["percdamp"],
+                                                           p["act_order"])
+                for nm in names:
+                    gq.gptq_quantize_layer(B[nm]["W"], None, 0, R=R, perm=perm, dead=dead, **p)
+            else:
+                gq.gptq_quantize_layer(B[names[0]]["W"], S, X.shape[0], **p)
+
+    for _ in range(warmup):
+        step()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        step()
+    torch.cuda.synchronize()
+    return (time.perf_counter() - t0) / steps
+
+
+def workloads(gq, torch, synth, names, dev):
+    """One timed line per extra workload (1 warm-up, 2 steps each)."""
+    out = {}
+    for name in names:
+        t0 = time.perf_counter()
+        if name == "tiny":
+            L = synth.tiny_layer(dev)
+            sec = time_layer(gq, torch, L["W"], L["X"], L["params"], 2, 1)
+            cfg = "tiny layer 128x256, 512 fp32 tokens, 4-bit per-row"
+        elif name in ("mlp_up", "mlp_down"):
+            P = synth.mlp_pair(dev)
+            L = P[name.split("_")[1]]
+            sec = time_layer(gq, torch, L["W"], L["X"], L["params"], 2, 1)
+            cfg = (f"MLP {name.split('_')[1]} {L['W'].shape[0]}x{L['W'].shape[1]}, "
+                   "262144 tokens, 3-bit g128 act-order")
+            del P
+        elif name.startswith("large_"):
+            which = name.split("_")[1]
+            L = synth.large_model_layer(which, dev)
+            sec = time_layer(gq, torch, L["W"], L["X"], L["params"], 2, 1)
+            cfg = f"d_model-12288 {which} {L['W'].shape[0]}x{L['W'].shape[1]}, 262144 tokens, 4-bit per-row"
+        elif name == "block":
+            B = synth.decoder_block(dev)
+            sec = time_block(gq, torch, B, 2, 1)
+            cfg = ("decoder block: q/k/v/o 4096x4096, gate/up 11008x4096, down 4096x11008, "
+                   "131072 tokens, 2-bit g64 act-order (seven linears)")
+            del B
+        else:
+            raise ValueError(name)
+        out[name] = {"s": round(sec, 5), "config": cfg,
+                     "wall_s_incl_inputs": round(time.perf_counter() - t0, 1)}
+        L = None
+        torch.cuda.empty_cache()
+        print(f"# workload {name}: {sec * 1e3:.2f} ms", file=sys.stderr, flush=True)
+    return out
+
+
+def phase_rooflines(ph, m, d, N, bits, gsize, bsize):
+    """Per-phase achieved rates against the published peaks, from the
+    library's per-phase event tracing (milliseconds per layer)."""
+    nb = -(-d // bsize)
+    ng = 1 if gsize == -1 else -(-d // gsize)
+    out = []
+    f_ms = ph["factor"]
+    out.append({"phase": "factor (fp64 reverse Cholesky + triangular inverse)",
+                "bound": "mfma", "unit": "TFLOP/s", "peak": PEAK_FP64_TFLOPS,
+                "algorithmic": f"2 d^3 / 3 = {2 * d ** 3 / 3:.4e} flop",
+                "ms": round(f_ms, 4),
+                "achieved": round(2 * d ** 3 / 3 / (f_ms * 1e-3) / 1e12, 2)})
+    # the column chain's contract bytes: the fp32 working block read, E
+    # written, the codes, R's diagonal blocks and the grids
+    chain_bytes = m * d * (4 + 4) + m * d * bits / 8 + nb * 128 * 128 * 4 + m * ng * 5
+    c_ms = ph["chain"]
+    out.append({"phase": "column chain (in-block quantize + OBS feedback)",
+                "bound": "hbm", "unit": "GB/s", "peak": PEAK_HBM_GBS,
+                "algorithmic": f"{chain_bytes:.4e} bytes (fp32 block in, E out, codes, R blocks, grids)",
+                "ms": round(c_ms, 4),
+                "achieved": round(chain_bytes / (c_ms * 1e-3) / 1e9, 1)})
+    lazy_flops = 2.0 * m * bsize * bsize * nb * (nb - 1) / 2.0
+    l_ms = ph["lazy"]
+    out.append({"phase": "lazy block update (fp32 MFMA)",
+                "bound": "mfma", "unit": "TFLOP/s", "peak": PEAK_FP32_TFLOPS,
+                "algorithmic": f"m b^2 n_b (n_b - 1) = {lazy_flops:.4e} flop",
+                "ms": round(l_ms, 4),
+                "achieved": round(lazy_flops / (l_ms * 1e-3) / 1e12, 2)})
+    for o in out:
+        o["frac"] = round(o["achieved"] / o["peak"], 4)
+    return out
 
 
 def main():
@@ -151,7 +319,7 @@ def main():
     evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
     t0 = time.perf_counter()
     for k in range(args.steps):
-        out = step(evs[k])
+        step(evs[k])
     torch.cuda.synchronize()
     elapsed = time.perf_counter() - t0
     if args.copy_probe_mib > 0:
@@ -187,6 +355,31 @@ def main():
         "phases_ms": {"hessian": round(hess_ms, 4), "quantize": round(quant_ms, 4)},
         "roofline": roofline,
     }
+    if args.phase == "layer":
+        # per-phase times from the library's event tracing (extra steps, not
+        # part of the headline timing)
+        gq.gptq_trace_enable(True)
+        gq.gptq_trace_read(reset=True)
+        for _ in range(2):
+            step()
+        torch.cuda.synchronize()
+        tr = gq.gptq_trace_read(reset=True)
+        gq.gptq_trace_enable(False)
+        ph = {k: v[0] / 2 for k, v in tr.items()}
+        line["phases_traced_ms"] = {k: round(v, 4) for k, v in ph.items()}
+        line["phase_rooflines"] = phase_rooflines(ph, m, d, N, params["bits"],
+                                                  params["group_size"], params["blocksize"])
+        line["inputs_sha256"] = {"W": tensor_sha(W), "X": tensor_sha(X)}
+    names = ([] if args.workloads == "none" or args.phase != "layer" else
+             ["tiny", "mlp_up", "mlp_down", "large_attn", "large_fc1", "large_fc2", "block"]
+             if args.workloads == "all" else args.workloads.split(","))
+    if names:
+        del S, hws, qws
+        Wc, Xc = W.cpu(), X.cpu()
+        del L, W, X
+        torch.cuda.empty_cache()
+        line["workloads"] = workloads(gq, torch, synth, names, dev)
+        W, X = Wc, Xc
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(W, X, params, N, args.cpu_tokens, args.cpu_rows)
     print(json.dumps(line), flush=True)

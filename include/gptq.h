@@ -297,6 +297,26 @@ gptq_status gptq_quantize_stack(const gptq_stack_layer* layers, int32_t n_layers
                                 void* X_out, double* layer_err, void* ws,
                                 size_t ws_bytes, void* stream);
 
+/* ---------------------------------------------------------------------------
+ * Tracing: per-phase GPU time.  While enabled, each launch group of a phase
+ * is bracketed by two hipEvents recorded on the caller's stream (a few
+ * microseconds per group; leave it off when timing the whole path).
+ * Phases: GPTQ_TRACE_STATS (the statistics kernels of one
+ * gptq_hessian_accumulate call), GPTQ_TRACE_FACTOR (one damping attempt's
+ * factorisation, H through R), GPTQ_TRACE_CHAIN (each in-block column-chain
+ * launch), GPTQ_TRACE_LAZY (each lazy block update), GPTQ_TRACE_OTHER (grid
+ * fits, working-copy set-up, output re-layout of a layer).
+ * gptq_trace_read waits for the recorded events and writes the summed
+ * milliseconds (and the number of launch groups) per phase since the last
+ * reset; reset = 1 clears them.  Host-side state guarded by a mutex.
+ * ------------------------------------------------------------------------- */
+#define GPTQ_TRACE_PHASES 5
+enum { GPTQ_TRACE_STATS = 0, GPTQ_TRACE_FACTOR = 1, GPTQ_TRACE_CHAIN = 2,
+       GPTQ_TRACE_LAZY = 3, GPTQ_TRACE_OTHER = 4 };
+gptq_status gptq_trace_enable(int32_t enable);
+gptq_status gptq_trace_read(double* ms /*[host] 5*/, int64_t* launches /*[host] 5, may be NULL*/,
+                            int32_t reset);
+
 #ifdef __cplusplus
 }
 #endif

@@ -547,7 +547,7 @@ def layer_error(W, W_hat, S, n: int) -> float:
     """(1/N) ||W X - W_hat X||_F^2 = (1/N) sum_r dw_r^T S dw_r   (eq. (6))."""
     dW = np.asarray(W, dtype=np.float64) - np.asarray(W_hat, dtype=np.float64)
     S = np.asarray(S, dtype=np.float64)
-    return float(np.einsum("rd,de,re->", dW, S, dW) / float(n))
+    return float(np.einsum("rd,de,re->", dW, S, dW, optimize=True) / float(n))
 
 
 def proxy_loss(rho_perm, R) -> float:

@@ -19,6 +19,7 @@ __all__ = [
     "gptq_cholesky_inverse", "gptq_quantize_layer", "gptq_workspace_bytes",
     "gptq_hessian_workspace_bytes", "gptq_factor_workspace_bytes",
     "gptq_hessian_accumulate_noalloc", "gptq_dequant_matmul", "gptq_quantize_stack",
+    "gptq_trace_enable", "gptq_trace_read", "TRACE_PHASES",
     "EXPORTED_SYMBOLS", "GRIDS", "ACTIVATIONS", "GPTQ_OK", "GPTQ_ERR_INVALID_ARG", "GPTQ_ERR_NOT_SPD",
     "GPTQ_ERR_WORKSPACE", "GPTQ_ERR_HIP",
 ]
@@ -32,8 +33,10 @@ EXPORTED_SYMBOLS = (
     "gptq_hessian_accumulate", "gptq_factor_workspace_bytes",
     "gptq_cholesky_inverse", "gptq_workspace_bytes", "gptq_quantize_layer",
     "gptq_hessian_accumulate_noalloc", "gptq_dequant_matmul",
-    "gptq_stack_workspace_bytes", "gptq_quantize_stack",
+    "gptq_stack_workspace_bytes", "gptq_quantize_stack", "gptq_trace_enable",
+    "gptq_trace_read",
 )
+TRACE_PHASES = ("stats", "factor", "chain", "lazy", "other")
 ACTIVATIONS = {"none": 0, "relu": 1, "silu": 2}
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -99,6 +102,11 @@ def load_library():
     lib.gptq_quantize_stack.restype = ctypes.c_int
     lib.gptq_quantize_stack.argtypes = [sp, i32, vp, i64, i32, vp,
                                         ctypes.POINTER(ctypes.c_double), vp, sz, vp]
+    lib.gptq_trace_enable.restype = ctypes.c_int
+    lib.gptq_trace_enable.argtypes = [i32]
+    lib.gptq_trace_read.restype = ctypes.c_int
+    lib.gptq_trace_read.argtypes = [ctypes.POINTER(ctypes.c_double),
+                                    ctypes.POINTER(ctypes.c_int64), i32]
     lib.gptq_factor_workspace_bytes.restype = sz
     lib.gptq_factor_workspace_bytes.argtypes = [i64]
     lib.gptq_cholesky_inverse.restype = ctypes.c_int
@@ -420,3 +428,16 @@ def gptq_quantize_stack(Ws, X: torch.Tensor, params, activation: str = "none",
                                  _stream(dev))
     _check(st, "gptq_quantize_stack")
     return dict(layers=outs, layer_err=[float(e) for e in errs], X_out=X_out)
+
+
+def gptq_trace_enable(enable: bool = True) -> None:
+    """Record per-phase GPU time (hipEvents around each launch group)."""
+    _check(_lib().gptq_trace_enable(int(bool(enable))), "gptq_trace_enable")
+
+
+def gptq_trace_read(reset: bool = True) -> dict:
+    """{phase: (milliseconds, launch groups)} since the last reset."""
+    ms = (ctypes.c_double * len(TRACE_PHASES))()
+    n = (ctypes.c_int64 * len(TRACE_PHASES))()
+    _check(_lib().gptq_trace_read(ms, n, int(bool(reset))), "gptq_trace_read")
+    return {p: (float(ms[i]), int(n[i])) for i, p in enumerate(TRACE_PHASES)}

@@ -91,8 +91,9 @@ __device__ inline void row_minmax(float& lo, float& hi) {
 // i0 + c uses static group perm[i0 + c] / gsize of scalesP / zerosP.
 // VEC: 0 = scalar global accesses, 1 = 16-byte ones, 2 = 16-byte ones and
 // a full 128-column block.
-// Stored codes: c = cz + z, or for signed grids (sgn) the low bits of
-// cz = c - z (two's complement, cmask = 2^b - 1).
+// Stored codes: c = cz + z, or for signed grids (sgn: the symmetric grid,
+// whose zero point is h = maxq / 2 everywhere) the low bits of c - h (two's
+// complement, cmask = 2^b - 1), converted on the way out.
 // The quotients w / Delta and rho / R_jj are products with fp32
 // reciprocals; they differ from the IEEE quotients by at most an ulp, which
 // can only matter within 1e-6 of a rounding boundary.
@@ -286,7 +287,7 @@ __global__ __launch_bounds__(256) void chain_kernel(
     const float cz = fminf(fmaxf(rintf(x * inv_scale), -zero), maxq - zero);
     const float e = fmaf(-scale, cz, x) * rinv[tk];
     if (q == qk) {
-      code[tk] = sgn ? static_cast<float>(static_cast<int>(cz) & cmask) : cz + zero;
+      code[tk] = cz + zero;
       eta[tk] = e;
     }
     const float eb = row_bcast(e, qk);
@@ -309,13 +310,16 @@ __global__ __launch_bounds__(256) void chain_kernel(
     for (int t = (tk > 4 ? tk : 4); t < kCols; ++t) w[t] = fmaf(-eb, rb[t - 4], w[t]);
   }
   }
-  // codes and residuals out through LDS, one coalesced run per column
+  // codes and residuals out through LDS, one coalesced run per column;
+  // signed grids (zero point h = maxq / 2 throughout) store c - h
   __syncthreads();
+  const int hz = static_cast<int>(maxq) / 2;
 #pragma unroll
   for (int t = 0; t < kCols; ++t) {
     const int cidx = q + kRowLanes * t;
     tile[cidx][rr] = eta[t];
-    ctile[cidx][rr] = static_cast<uint8_t>(code[t]);
+    const int c = static_cast<int>(code[t]);
+    ctile[cidx][rr] = static_cast<uint8_t>(sgn ? ((c - hz) & cmask) : c);
   }
   __syncthreads();
   {

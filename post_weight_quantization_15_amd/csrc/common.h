@@ -166,6 +166,13 @@ gptq_status launch_dequant_matmul(const uint16_t* X, int64_t ldx, int64_t n,
                                   int64_t ldy, int out_bf16, int act,
                                   hipStream_t st);
 
+// Tracing (trace.hip): per-phase event pairs on the caller's stream while
+// enabled.  trace_begin returns a token (-1 when off) for trace_end.
+constexpr int kTracePhases = GPTQ_TRACE_PHASES;
+bool trace_on();
+int trace_begin(hipStream_t st, int phase);
+void trace_end(hipStream_t st, int token);
+
 // Layer error (1/n) sum_r (W - W_hat)_r^T S (W - W_hat)_r into *out (fp64);
 // part: layer_error_part_count(m, d) doubles of scratch.
 size_t layer_error_part_count(int64_t m, int64_t d);

@@ -147,11 +147,14 @@ gptq_status enqueue_factor(const float* S, int64_t n, int64_t d, float percdamp,
                            int act_order, int attempt, float* R, int32_t* perm,
                            uint8_t* dead, const FactorWs& f, hipStream_t st) {
   gptq_status s;
+  const int tk = trace_begin(st, GPTQ_TRACE_FACTOR);
   if ((s = launch_prep_stats(S, d, n, percdamp, attempt, f, dead, st)) != GPTQ_OK) return s;
   if (attempt == 0 && (s = launch_perm(d, act_order, f, perm, st)) != GPTQ_OK) return s;
   if ((s = launch_build_h(S, d, n, perm, dead, f, st)) != GPTQ_OK) return s;
   if ((s = launch_factor_inverse(d, f, st)) != GPTQ_OK) return s;
-  return launch_r_to_f32(d, f, R, st);
+  s = launch_r_to_f32(d, f, R, st);
+  trace_end(st, tk);
+  return s;
 }
 
 // Waits for the stream and reads the attempt's outcome.
@@ -192,6 +195,7 @@ gptq_status enqueue_columns(const void* W, gptq_dtype w_dtype, int64_t m,
                             uint32_t* qweight, float* scales, uint8_t* zeros,
                             int32_t* g_idx, float* w_hat, hipStream_t st) {
   gptq_status s;
+  int tk = trace_begin(st, GPTQ_TRACE_OTHER);
   const int64_t gsize = p->group_size;
   const bool sym = p->grid == GPTQ_GRID_SYMMETRIC;
   const bool stat = static_grids(p);
@@ -212,6 +216,7 @@ gptq_status enqueue_columns(const void* W, gptq_dtype w_dtype, int64_t m,
     return s;
   const int bi = internal_block(d, p);
   if ((s = launch_rbt(Ru, d, bi, q.RbT, st)) != GPTQ_OK) return s;
+  trace_end(st, tk);
   // Lazy batches of nb blocks: each block's chain first applies the batch's
   // earlier residuals to its own columns, and one update per batch carries
   // the whole batch to the columns after it (the same sums regrouped, as
@@ -246,15 +251,23 @@ gptq_status enqueue_columns(const void* W, gptq_dtype w_dtype, int64_t m,
       a.E = q.E + (i0 - s0) * m;
       a.sb0 = s0;
       a.kn = static_cast<int>(i0 - s0);
+      tk = trace_begin(st, GPTQ_TRACE_CHAIN);
       if ((s = launch_chain(a, st)) != GPTQ_OK) return s;
+      trace_end(st, tk);
     }
     const int kw = static_cast<int>(std::min<int64_t>(int64_t(nb) * bi, d - s0));
-    if ((s = launch_lazy_update(q.WT, m, d, Ru, s0, kw, q.E, st)) != GPTQ_OK)
-      return s;
+    if (d - s0 - kw > 0) {
+      tk = trace_begin(st, GPTQ_TRACE_LAZY);
+      if ((s = launch_lazy_update(q.WT, m, d, Ru, s0, kw, q.E, st)) != GPTQ_OK) return s;
+      trace_end(st, tk);
+    }
   }
-  return launch_outputs(m, d, p->bits, static_cast<int>(gsize), sym, stat,
-                        q.codesP, q.scalesP, q.zerosP, q.pinv, q.codesO,
-                        qweight, scales, zeros, g_idx, w_hat, st);
+  tk = trace_begin(st, GPTQ_TRACE_OTHER);
+  s = launch_outputs(m, d, p->bits, static_cast<int>(gsize), sym, stat, q.codesP,
+                     q.scalesP, q.zerosP, q.pinv, q.codesO, qweight, scales, zeros,
+                     g_idx, w_hat, st);
+  trace_end(st, tk);
+  return s;
 }
 
 constexpr int64_t kMaxStackTokens = int64_t(65535) * 8;   // dequant grid.y
@@ -343,8 +356,11 @@ gptq_status gptq_hessian_accumulate(float* S, int64_t d, const void* X,
   if (n_tok > 0 && !X) return GPTQ_ERR_INVALID_ARG;
   const size_t need = hessian_ws_bytes(d, n_tok);
   if (ws_bytes < need || (need > 0 && !ws)) return GPTQ_ERR_WORKSPACE;
-  return launch_hessian(S, d, X, x_dtype, n_tok, ldx, ws,
-                        static_cast<hipStream_t>(stream));
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  const int tk = trace_begin(st, GPTQ_TRACE_STATS);
+  const gptq_status s = launch_hessian(S, d, X, x_dtype, n_tok, ldx, ws, st);
+  trace_end(st, tk);
+  return s;
 }
 
 gptq_status gptq_hessian_accumulate_noalloc(float* S, int64_t d, const void* X,
@@ -361,7 +377,10 @@ gptq_status gptq_hessian_accumulate_noalloc(float* S, int64_t d, const void* X,
   void* ws = nullptr;
   gptq_status s;
   if ((s = scratch_address(st, &ws)) != GPTQ_OK) return s;
-  return launch_hessian(S, d, X, x_dtype, n_tok, ldx, ws, st, cap);
+  const int tk = trace_begin(st, GPTQ_TRACE_STATS);
+  s = launch_hessian(S, d, X, x_dtype, n_tok, ldx, ws, st, cap);
+  trace_end(st, tk);
+  return s;
 }
 
 gptq_status gptq_dequant_matmul(const void* X, gptq_dtype x_dtype, int64_t n,

@@ -237,3 +237,17 @@ def test_stack_rejects(lib):
     assert lib.gptq_stack_workspace_bytes(badp, 1, 1000) == 0
     assert lib.gptq_quantize_stack(two, 2, FAKE, 1000, 0, FAKE, None, FAKE, 16,
                                    None) == gq.GPTQ_ERR_WORKSPACE
+
+
+def test_trace_host_side(lib):
+    """Tracing state is host-side: enabling, reading with nothing recorded
+    and rejecting bad arguments need no GPU."""
+    import ctypes as C
+    ms = (C.c_double * 5)()
+    n = (C.c_int64 * 5)()
+    assert lib.gptq_trace_enable(2) == gq.GPTQ_ERR_INVALID_ARG
+    assert lib.gptq_trace_read(None, None, 0) == gq.GPTQ_ERR_INVALID_ARG
+    assert lib.gptq_trace_read(ms, n, 1) == gq.GPTQ_OK
+    assert lib.gptq_trace_read(ms, n, 0) == gq.GPTQ_OK and list(n) == [0] * 5
+    assert lib.gptq_trace_enable(1) == gq.GPTQ_OK
+    assert lib.gptq_trace_enable(0) == gq.GPTQ_OK

@@ -172,6 +172,27 @@ def check_R_identity(R_gpu, S_gpu, n, perm, dead, damp, rng, nrows=64):
     return err
 
 
+def oracle_factor_tie_forced(S_o, n, params, perm_gpu):
+    """The oracle's factor from its own S.  Act-order is a decision taken
+    from floating point (a sort of diag H): where the GPU's order differs
+    from the oracle's, every difference must be between features whose
+    oracle keys agree within the statistics' rounding bound (the entrywise
+    bound on S), and the oracle then takes the GPU's order, as it takes the
+    GPU's code at a near-tie.  Returns (perm, dead, R, forced swaps)."""
+    H, perm_o, dead_o, damp_o = orc.prepare(S_o, n, params["percdamp"], params["act_order"])
+    if np.array_equal(perm_o, perm_gpu) or not params["act_order"]:
+        R_o, _ = orc.factor(H, damp_o)
+        return perm_o, dead_o, R_o, 0
+    H0, _, dead_o, damp_o = orc.prepare(S_o, n, params["percdamp"], False)
+    keys = np.diag(H0)
+    kg = keys[perm_gpu]
+    tol = chain_steps(S_o.shape[0], n) * 2.0 ** -24 * 2
+    assert np.all(kg[1:] <= kg[:-1] * (1 + tol)), "GPU act-order is not a near-tie reordering"
+    swaps = int(np.sum(perm_o != perm_gpu))
+    R_o, _ = orc.factor(H0[np.ix_(perm_gpu, perm_gpu)], damp_o)
+    return np.asarray(perm_gpu), dead_o, R_o, swaps
+
+
 def oracle_rows(W_rows, perm, dead, R, params):
     """The oracle's column loop on some rows, given the factor: the steps of
     orc.gptq_layer after its factorisation."""
@@ -275,10 +296,8 @@ def independent_layer(tag, W, X, params, S=None, factor=None, cache=None):
         cache["r_err"] = check_R_entrywise(R, R_g)
         print(f"{tag}: R checked {cache['r_err']}", flush=True)
         del R_g, H, R
-        H_o, perm_o, dead_o, damp_o = orc.prepare(S_o, n, params["percdamp"],
-                                                  params["act_order"])
-        R_o, _ = orc.factor(H_o, damp_o)
-        cache.update(S_o=S_o, R_o=R_o, perm_o=perm_o, dead_o=dead_o)
+        perm_o, dead_o, R_o, swaps = oracle_factor_tie_forced(S_o, n, params, perm_g)
+        cache.update(S_o=S_o, R_o=R_o, perm_o=perm_o, dead_o=dead_o, perm_swaps=swaps)
     out = gpu_layer(W, S, n, params, factor)
 
     def res_fn(W64):
@@ -286,7 +305,8 @@ def independent_layer(tag, W, X, params, S=None, factor=None, cache=None):
 
     rep = compare_rows(out, W, cache["S_o"], n, params, res_fn, tag=tag)
     record(tag, S_entry_err=cache["s_err"], R_entry_err=cache["r_err"][0],
-           R_fro_err=cache["r_err"][1], independent=True, **summary(rep))
+           R_fro_err=cache["r_err"][1], act_order_forced_swaps=cache["perm_swaps"],
+           independent=True, **summary(rep))
     return S
 
 
