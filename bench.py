@@ -164,6 +164,12 @@ def time_layer(gq, torch, W, X, params, steps, warmup, shared=None):
         gq.gptq_hessian_accumulate(S, X, ws=hws)
         return gq.gptq_quantize_layer(W, S, N, ws=qws, **params)
 
+    return timed_and_traced(gq, torch, step, steps, warmup)
+
+
+def timed_and_traced(gq, torch, step, steps, warmup):
+    """Seconds per step over `steps` untraced steps after `warmup`, then one
+    traced step for the per-phase split (milliseconds per phase)."""
     for _ in range(warmup):
         step()
     torch.cuda.synchronize()
@@ -171,7 +177,14 @@ def time_layer(gq, torch, W, X, params, steps, warmup, shared=None):
     for _ in range(steps):
         step()
     torch.cuda.synchronize()
-    return (time.perf_counter() - t0) / steps
+    sec = (time.perf_counter() - t0) / steps
+    gq.gptq_trace_enable(True)
+    gq.gptq_trace_read(reset=True)
+    step()
+    torch.cuda.synchronize()
+    tr = gq.gptq_trace_read(reset=True)
+    gq.gptq_trace_enable(False)
+    return sec, {k: round(v[0], 3) for k, v in tr.items()}
 
 
 def time_block(gq, torch, B, steps, warmup):
@@ -198,14 +211,7 @@ def time_block(gq, torch, B, steps, warmup):
             else:
                 gq.gptq_quantize_layer(B[names[0]]["W"], S, X.shape[0], **p)
 
-    for _ in range(warmup):
-        step()
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for _ in range(steps):
-        step()
-    torch.cuda.synchronize()
-    return (time.perf_counter() - t0) / steps
+    return timed_and_traced(gq, torch, step, steps, warmup)
 
 
 def workloads(gq, torch, synth, names, dev):
@@ -215,29 +221,29 @@ def workloads(gq, torch, synth, names, dev):
         t0 = time.perf_counter()
         if name == "tiny":
             L = synth.tiny_layer(dev)
-            sec = time_layer(gq, torch, L["W"], L["X"], L["params"], 2, 1)
+            sec, ph = time_layer(gq, torch, L["W"], L["X"], L["params"], 2, 1)
             cfg = "tiny layer 128x256, 512 fp32 tokens, 4-bit per-row"
         elif name in ("mlp_up", "mlp_down"):
             P = synth.mlp_pair(dev)
             L = P[name.split("_")[1]]
-            sec = time_layer(gq, torch, L["W"], L["X"], L["params"], 2, 1)
+            sec, ph = time_layer(gq, torch, L["W"], L["X"], L["params"], 2, 1)
             cfg = (f"MLP {name.split('_')[1]} {L['W'].shape[0]}x{L['W'].shape[1]}, "
                    "262144 tokens, 3-bit g128 act-order")
             del P
         elif name.startswith("large_"):
             which = name.split("_")[1]
             L = synth.large_model_layer(which, dev)
-            sec = time_layer(gq, torch, L["W"], L["X"], L["params"], 2, 1)
+            sec, ph = time_layer(gq, torch, L["W"], L["X"], L["params"], 2, 1)
             cfg = f"d_model-12288 {which} {L['W'].shape[0]}x{L['W'].shape[1]}, 262144 tokens, 4-bit per-row"
         elif name == "block":
             B = synth.decoder_block(dev)
-            sec = time_block(gq, torch, B, 2, 1)
+            sec, ph = time_block(gq, torch, B, 2, 1)
             cfg = ("decoder block: q/k/v/o 4096x4096, gate/up 11008x4096, down 4096x11008, "
                    "131072 tokens, 2-bit g64 act-order (seven linears)")
             del B
         else:
             raise ValueError(name)
-        out[name] = {"s": round(sec, 5), "config": cfg,
+        out[name] = {"s": round(sec, 5), "config": cfg, "phases_traced_ms": ph,
                      "wall_s_incl_inputs": round(time.perf_counter() - t0, 1)}
         L = None
         torch.cuda.empty_cache()

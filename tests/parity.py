@@ -121,7 +121,7 @@ def unsigned_codes(stored, zeros_used, g_idx, bits, signed):
     return s + zeros_used[np.arange(stored.shape[0])[:, None], g_idx[None, :]]
 
 
-def compare_layer(res, W, S, n, gpu, params, check_w_hat=True):
+def compare_layer(res, W, S, n, gpu, params, check_w_hat=True, strict=True):
     """Full comparison of one quantized layer (or a sample of its rows: rows
     are independent given R and their grids).
 
@@ -135,7 +135,8 @@ def compare_layer(res, W, S, n, gpu, params, check_w_hat=True):
     tie-forced oracle (see ``replay``), which is the independent oracle
     except where the tolerance admits another rounding; the same figures
     against the independent oracle are reported, and enforced on each row's
-    prefix before its first divergence.
+    prefix before its first divergence.  With strict=False nothing is
+    raised: the report lists what failed under "problems".
     """
     bits, g, b = params["bits"], params["group_size"], params["blocksize"]
     symmetric = params.get("grid", "minmax") == "symmetric"
@@ -248,5 +249,6 @@ def compare_layer(res, W, S, n, gpu, params, check_w_hat=True):
         problems.append(f"||W_hat - W_hat_tf||/||W_hat_tf|| = {rel_w_tf}")
     if rel_L > 1e-3:
         problems.append(f"layer error rel diff {rel_L}")
-    assert not problems, f"{problems} {report}"
+    report["problems"] = problems
+    assert not (strict and problems), f"{problems} {report}"
     return report
