@@ -64,13 +64,25 @@ __device__ inline float row_bcast(float x, int src) {
   return x;
 }
 
-// min / max over the 16 lanes of a row
+// min / max over the 16 lanes of a row, by DPP inside the row: mirror
+// (lane i with 15 - i), half mirror (i with 7 - i in each half of 8), then
+// the two swaps inside each quad; after the second step each quad's four
+// lanes together hold all sixteen values.  min and max are exact, so the
+// order of the combination does not change the result.
+template <int CTRL>
+__device__ inline float row_dpp(float x) {
+  return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), CTRL, 0xF, 0xF, true));
+}
+
 __device__ inline void row_minmax(float& lo, float& hi) {
-#pragma unroll
-  for (int o = 1; o < kRowLanes; o <<= 1) {
-    lo = fminf(lo, __shfl_xor(lo, o));
-    hi = fmaxf(hi, __shfl_xor(hi, o));
-  }
+  lo = fminf(lo, row_dpp<0x140>(lo));   // row_mirror
+  hi = fmaxf(hi, row_dpp<0x140>(hi));
+  lo = fminf(lo, row_dpp<0x141>(lo));   // row_half_mirror
+  hi = fmaxf(hi, row_dpp<0x141>(hi));
+  lo = fminf(lo, row_dpp<0x4E>(lo));    // quad_perm [2, 3, 0, 1]
+  hi = fmaxf(hi, row_dpp<0x4E>(hi));
+  lo = fminf(lo, row_dpp<0xB1>(lo));    // quad_perm [1, 0, 3, 2]
+  hi = fmaxf(hi, row_dpp<0xB1>(hi));
 }
 
 // One block [i0, i0 + bw) of the column loop for 16 output rows per
@@ -86,18 +98,21 @@ __device__ inline void row_minmax(float& lo, float& hi) {
 // multiples of FS.  A group that starts inside the block ends inside it
 // (checked on the host), so every fit sees fully compensated columns; a
 // group that starts at the block start and reaches past it also reads its
-// later columns from WT (compensated by every earlier block).
+// later columns from WT (compensated by every earlier block).  EXACT: the
+// groups are FS columns long and the block starts on a group boundary.
 // FS == kFsRow: the row's grid (scalesP row 0).  FS == kFsStatic: column
 // i0 + c uses static group perm[i0 + c] / gsize of scalesP / zerosP.
-// VEC: 0 = scalar global accesses, 1 = 16-byte ones, 2 = 16-byte ones and
-// a full 128-column block.
+// VEC: 0 = scalar global accesses, 1 = 16-byte ones (m % 4 == 0, WT and E
+// 16-byte aligned, codes 4-byte aligned), 2 = 16-byte ones and a full
+// 128-column block.  The R block is copied into LDS 16 bytes per lane in
+// every mode (RL is 16-byte aligned).
 // Stored codes: c = cz + z, or for signed grids (sgn: the symmetric grid,
 // whose zero point is h = maxq / 2 everywhere) the low bits of c - h (two's
 // complement, cmask = 2^b - 1), converted on the way out.
 // The quotients w / Delta and rho / R_jj are products with fp32
 // reciprocals; they differ from the IEEE quotients by at most an ulp, which
 // can only matter within 1e-6 of a rounding boundary.
-template <int FS, int VEC>
+template <int FS, int VEC, bool EXACT>
 __global__ __launch_bounds__(256) void chain_kernel(
     const float* __restrict__ WT, int64_t m, int64_t d, const float* __restrict__ RL,
     int64_t i0, int bw_arg, int bi, float maxq, int64_t gsize, int sym, int sgn,
@@ -109,7 +124,7 @@ __global__ __launch_bounds__(256) void chain_kernel(
   constexpr int kSg = FS == kFsStatic ? kB : 1;
   __shared__ __attribute__((aligned(16))) float rl[kB * kB];
   __shared__ float tile[kB][kTp];
-  __shared__ uint8_t ctile[kB][kChainRows];
+  __shared__ __attribute__((aligned(16))) uint8_t ctile[kB][kChainRows];
   __shared__ float sgs[kSg][kChainRows], sgz[kSg][kChainRows], sgi[kSg][kChainRows];
   const int tid = threadIdx.x;
   const int rr = tid >> 4, q = tid & 15;
@@ -120,13 +135,19 @@ __global__ __launch_bounds__(256) void chain_kernel(
   // stage RL of this block (contiguous 64 KiB) and the block's columns of the
   // workgroup's rows (one 64-byte run per column)
   {
-    const f32x4* src = reinterpret_cast<const f32x4*>(RL + (i0 / bi) * int64_t(kB) * kB);
-    f32x4* dst = reinterpret_cast<f32x4*>(rl);
-    f32x4 buf[kB * kB / 4 / 256];
+    // straight into LDS, no registers: each wave instruction copies 1 KiB,
+    // lane l taking its bytes 16 l .. 16 l + 15
+    typedef const void __attribute__((address_space(1)))* gvoid;
+    typedef void __attribute__((address_space(3)))* lvoid;
+    const char* src = reinterpret_cast<const char*>(RL + (i0 / bi) * int64_t(kB) * kB);
+    char* dst = reinterpret_cast<char*>(rl);
+    const int wv = tid >> 6, ln = tid & 63;
 #pragma unroll
-    for (int u = 0; u < kB * kB / 4 / 256; ++u) buf[u] = src[tid + 256 * u];
-#pragma unroll
-    for (int u = 0; u < kB * kB / 4 / 256; ++u) dst[tid + 256 * u] = buf[u];
+    for (int u = 0; u < kB * kB / 4 / 256; ++u) {
+      const int chunk = u * 256 + wv * 64;
+      __builtin_amdgcn_global_load_lds((gvoid)(src + 16 * (chunk + ln)), (lvoid)(dst + 16 * chunk),
+                                       16, 0, 0);
+    }
   }
   {
     const int c = tid >> 1, h = tid & 1;
@@ -167,6 +188,9 @@ __global__ __launch_bounds__(256) void chain_kernel(
       sgi[c][row] = 1.0f / s;
     }
   }
+  // the direct copies into LDS are counted by vmcnt, which the barrier does
+  // not wait for
+  __builtin_amdgcn_s_waitcnt((0 & 15) | ((0 >> 4) << 14) | (7 << 4) | (15 << 8));
   __syncthreads();
   if (kn > 0) {
     // the earlier blocks of this lazy batch, not yet applied to WT:
@@ -255,7 +279,7 @@ __global__ __launch_bounds__(256) void chain_kernel(
       zero = sgz[k][rr];
       inv_scale = sgi[k][rr];
     }
-    if (FS > 0 && k % (FS > 0 ? FS : 1) == 0 && (i0 + k) % gsize == 0) {
+    if (FS > 0 && k % (FS > 0 ? FS : 1) == 0 && (EXACT || (i0 + k) % gsize == 0)) {
       const int64_t col = i0 + k;
       const int64_t gend = min(col + gsize, d);
       float lo = 0.0f, hi = 0.0f;
@@ -267,7 +291,8 @@ __global__ __launch_bounds__(256) void chain_kernel(
           hi = fmaxf(hi, w[t]);
         }
       }
-      for (int64_t cc = i0 + bw + q; cc < gend; cc += kRowLanes) {
+      // (only a group that starts at the block start can reach past it)
+      for (int64_t cc = i0 + bw + q; k == 0 && cc < gend; cc += kRowLanes) {
         const float x = WT[cc * m + rs];
         lo = fminf(lo, x);
         hi = fmaxf(hi, x);
@@ -280,11 +305,12 @@ __global__ __launch_bounds__(256) void chain_kernel(
         zerosP[(col / gsize) * m + r] = static_cast<uint8_t>(zero);
       }
     }
-    // c - z = clamp(rint(x / scale), -z, maxq - z) (small integers, exact),
+    // c - z = clamp(rint(x / scale), -z, maxq - z) (small integers, exact;
+    // the clamp as one median-of-three),
     // and w - q = x - scale (c - z) in one rounding: six dependent
     // operations from the column's value to its residual
     const float x = w[tk];
-    const float cz = fminf(fmaxf(rintf(x * inv_scale), -zero), maxq - zero);
+    const float cz = __builtin_amdgcn_fmed3f(rintf(x * inv_scale), -zero, maxq - zero);
     const float e = fmaf(-scale, cz, x) * rinv[tk];
     if (q == qk) {
       code[tk] = cz + zero;
@@ -322,7 +348,21 @@ __global__ __launch_bounds__(256) void chain_kernel(
     ctile[cidx][rr] = static_cast<uint8_t>(sgn ? ((c - hz) & cmask) : c);
   }
   __syncthreads();
-  {
+  if (VEC && r0 + kChainRows <= m) {
+    // four lanes per column, consecutive lanes on consecutive addresses:
+    // 16-byte runs of E and 4-byte runs of codes (m % 4 == 0 here)
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+      const int e = tid + 256 * u;
+      const int c = e >> 2, p4 = 4 * (e & 3);
+      if (c < bw) {
+        const f32x4 v = {tile[c][p4], tile[c][p4 + 1], tile[c][p4 + 2], tile[c][p4 + 3]};
+        *reinterpret_cast<f32x4*>(E + int64_t(c) * m + r0 + p4) = v;
+        *reinterpret_cast<uint32_t*>(codesP + (i0 + c) * m + r0 + p4) =
+            *reinterpret_cast<const uint32_t*>(&ctile[c][p4]);
+      }
+    }
+  } else {
     const int c = tid >> 1, h = tid & 1;
     if (c < bw) {
       float* erow = E + int64_t(c) * m + r0 + 8 * h;
@@ -337,21 +377,36 @@ __global__ __launch_bounds__(256) void chain_kernel(
   }
 }
 
-// Launches chain_kernel<FS, VEC> for the VEC the arguments allow.
+// Launches chain_kernel<FS, VEC, EXACT> for the VEC and EXACT the
+// arguments allow.
 template <int FS>
 gptq_status launch_fs(const ChainArgs& a, hipStream_t st) {
-  const bool vec = a.m % 4 == 0 && reinterpret_cast<uintptr_t>(a.WT) % 16 == 0;
+  const bool vec = a.m % 4 == 0 && reinterpret_cast<uintptr_t>(a.WT) % 16 == 0 &&
+                   reinterpret_cast<uintptr_t>(a.E) % 16 == 0 &&
+                   reinterpret_cast<uintptr_t>(a.codesP) % 4 == 0;
   const dim3 grid(static_cast<unsigned>((a.m + kChainRows - 1) / kChainRows));
-#define GPTQ_CHAIN(V)                                                            \
-  chain_kernel<FS, V><<<grid, 256, 0, st>>>(                                      \
+  // groups of exactly FS columns starting on an FS boundary: every FS-th
+  // block column starts a group, known at compile time (the fits are then
+  // straight-line code, which keeps the column loop free of branches)
+  const bool exact = FS > 0 && a.gsize == FS && a.i0 % FS == 0;
+#define GPTQ_CHAIN(V, X)                                                         \
+  chain_kernel<FS, V, X><<<grid, 256, 0, st>>>(                                   \
       a.WT, a.m, a.d, a.RL, a.i0, a.bw, a.bi, a.maxq, a.gsize, a.sym, a.sgn,     \
       a.cmask, a.perm, a.scalesP, a.zerosP, a.codesP, a.E, a.R, a.sb0, a.kn, a.Esb)
-  if (vec && a.bw == kB)
-    GPTQ_CHAIN(2);
-  else if (vec)
-    GPTQ_CHAIN(1);
-  else
-    GPTQ_CHAIN(0);
+  if (vec && a.bw == kB) {
+    if constexpr (FS > 0) {
+      if (exact)
+        GPTQ_CHAIN(2, true);
+      else
+        GPTQ_CHAIN(2, false);
+    } else {
+      GPTQ_CHAIN(2, false);
+    }
+  } else if (vec) {
+    GPTQ_CHAIN(1, false);
+  } else {
+    GPTQ_CHAIN(0, false);
+  }
 #undef GPTQ_CHAIN
   GPTQ_CHECK_LAUNCH();
   return GPTQ_OK;

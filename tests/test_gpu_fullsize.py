@@ -278,12 +278,14 @@ def compare_rows(out, W, n, params, routes, rows=None, batch=1024, tag="",
     every batch is a complete comparison; a batch meeting the 1e-3 bounds on
     dequantized weights and layer error makes their sums meet them too).
 
-    routes: name -> (res_fn, S, strict): res_fn(W rows) runs the oracle's
-    loop from one set of stage inputs, S is the statistics the layer error
-    is measured with, strict makes any failure raise.  control = (a, b)
-    also compares route b's oracle result with route a's by the same rules
-    (the oracle against itself on the two inputs).  Returns the whole-layer
-    figures per route (and "control")."""
+    routes: name -> (res_fn, S, strict[, nrows]): res_fn(W rows) runs the
+    oracle's loop from one set of stage inputs, S is the statistics the
+    layer error is measured with, strict makes any failure raise, nrows
+    (default all) limits the route to the first nrows of `rows`.
+    control = (a, b) also compares route b's oracle result with route a's
+    by the same rules (the oracle against itself on the two inputs), on the
+    rows both routes cover.  Returns the whole-layer figures per route (and
+    "control")."""
     m, d = W.shape
     rows = np.arange(m) if rows is None else rows
     tot = {k: _agg_start() for k in routes}
@@ -296,11 +298,14 @@ def compare_rows(out, W, n, params, routes, rows=None, batch=1024, tag="",
                for k, v in out.items()}
         W64 = np64(W.index_select(0, ridx))
         res = {}
-        for name, (res_fn, S_r, strict) in routes.items():
+        for name, route in routes.items():
+            res_fn, S_r, strict = route[:3]
+            if len(route) > 3 and route[3] is not None and b0 >= route[3]:
+                continue
             res[name] = res_fn(W64)
             rep = compare_layer(res[name], W64, S_r, n, gpu, params, strict=strict)
             _agg_add(tot[name], rep)
-        if control is not None:
+        if control is not None and all(k in res for k in control):
             a, b = control
             rep = compare_layer(res[b], W64, routes[b][1], n, as_gpu_dict(res[a], params),
                                 params, check_w_hat=False, strict=False)
@@ -316,7 +321,7 @@ def record(tag, **kw):
 
 
 def independent_layer(tag, W, X, params, S=None, factor=None, cache=None,
-                      gate_from_x=True):
+                      gate_from_x=True, from_x_rows=None):
     """d = 4096, every row, along two routes:
       * same_S (gating): the oracle's own prepare, factor and loop on the
         GPU's S -- each stage against the oracle given the same input, with
@@ -327,7 +332,8 @@ def independent_layer(tag, W, X, params, S=None, factor=None, cache=None,
         band of every decision (gate_from_x); reported otherwise, beside the
         control: the oracle's same_S result against its from_X result by the
         same rules, which measures how far that rounding alone moves the
-        loop.
+        loop.  from_x_rows limits from_X and the control to the first rows
+        (every row when None).
     `cache` keeps the statistics-side results for layers sharing one
     input."""
     n, d = X.shape
@@ -359,7 +365,7 @@ def independent_layer(tag, W, X, params, S=None, factor=None, cache=None,
         "same_S": (lambda W64: oracle_rows(W64, c["perm_g"], c["dead_g"], c["R_g"], params),
                    c["S64"], True),
         "from_X": (lambda W64: oracle_rows(W64, c["perm_o"], c["dead_o"], c["R_o"], params),
-                   c["S_o"], gate_from_x),
+                   c["S_o"], gate_from_x, from_x_rows),
     }
     rep = compare_rows(out, W, n, params, routes, tag=tag, control=("same_S", "from_X"))
     record(tag, S_entry_err=cache["s_err"], R_entry_err=cache["r_err"][0],
@@ -434,9 +440,9 @@ def test_mlp_down_full(dev):
                     np.random.default_rng(12), nrows=1024)
 
 
-def test_decoder_block_attention_full(dev):
-    """q/k/v on one shared factor and o on its own, 2-bit g64, act-order,
-    131072 tokens; every row against the independent oracle."""
+def test_decoder_block_qkv_full(dev):
+    """q/k/v (4096 x 4096) on one shared factor, 2-bit g64, act-order,
+    131072 tokens; every row along both routes."""
     B = synth.decoder_block(dev)
     p = B["q"]["params"]
     X = B["q"]["X"]
@@ -447,14 +453,18 @@ def test_decoder_block_attention_full(dev):
     for nm in ("q", "k", "v"):
         independent_layer(f"block_{nm}", B[nm]["W"], X, p, S=S, factor=(Rt, pt, dt),
                           cache=cache, gate_from_x=False)
-    del S, Rt, cache
+
+
+def test_decoder_block_o_full(dev):
+    """o (4096 x 4096) on the attention output; every row, both routes."""
+    B = synth.decoder_block(dev)
     independent_layer("block_o", B["o"]["W"], B["o"]["X"], B["o"]["params"],
                       gate_from_x=False)
 
 
-def test_decoder_block_mlp_full(dev):
-    """gate and up (11008 x 4096) on one shared factor, and down
-    (4096 x 11008, 1024 sampled rows)."""
+def test_decoder_block_gate_up_full(dev):
+    """gate and up (11008 x 4096) on one shared factor: every row on the
+    same S, the first 4096 rows also from X with the control."""
     B = synth.decoder_block(dev)
     p = B["gate"]["params"]
     X = B["gate"]["X"]
@@ -464,8 +474,12 @@ def test_decoder_block_mlp_full(dev):
     cache = {}
     for nm in ("gate", "up"):
         independent_layer(f"block_{nm}", B[nm]["W"], X, p, S=S, factor=(Rt, pt, dt),
-                          cache=cache, gate_from_x=False)
-    del S, Rt, cache
+                          cache=cache, gate_from_x=False, from_x_rows=4096)
+
+
+def test_decoder_block_down_full(dev):
+    """down (4096 x 11008) on the SiLU-gated input, 1024 sampled rows."""
+    B = synth.decoder_block(dev)
     stagewise_layer("block_down", B["down"]["W"], B["down"]["X"], B["down"]["params"],
                     np.random.default_rng(13), nrows=1024)
 
