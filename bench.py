@@ -251,6 +251,81 @@ def workloads(gq, torch, synth, names, dev):
     return out
 
 
+def _event_ms(torch, fn, reps):
+    """Mean milliseconds of fn() over reps calls, HIP events on the current
+    stream (the one the library launches on)."""
+    fn()
+    torch.cuda.synchronize()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(reps):
+        fn()
+    e1.record()
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) / reps
+
+
+def next_rows(gq, torch, synth, dev):
+    """The rows after the core path, each timed: the dequantizing matmul
+    against HBM (the packed weights are its traffic), the quantizer variants
+    and the layer-by-layer driver on the attention-projection shape."""
+    out = {}
+    # ---- dequantizing matmul: fc1-shaped weights (49152 x 12288), random
+    # codes (the kernel's time does not depend on their values)
+    m, d, g = 49152, 12288, 128
+    ng = d // g
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(7)
+    dq = []
+    for bits in (4, 3, 2):
+        words = -(-d * bits // 32)
+        qw = torch.randint(-2 ** 31, 2 ** 31 - 1, (m, words), dtype=torch.int32,
+                           device=dev, generator=gen)
+        sc32 = torch.rand(m, ng, device=dev, generator=gen) * 0.01 + 0.001
+        zp = torch.randint(0, 2 ** bits, (m, ng), dtype=torch.uint8, device=dev,
+                           generator=gen)
+        gi = (torch.arange(d, device=dev) // g).to(torch.int32)
+        for n in (1, 8):
+            X = torch.randn(n, d, device=dev, generator=gen).to(torch.bfloat16)
+            Y = torch.empty(n, m, device=dev)
+            for sc in (sc32, sc32.half()):
+                ms = _event_ms(torch, lambda: gq.gptq_dequant_matmul(X, qw, sc, zp, gi, bits, g,
+                                                                    Y=Y), 20)
+                byts = (qw.numel() * 4 + sc.numel() * sc.element_size() + zp.numel() + gi.numel() * 4
+                        + X.numel() * 2 + Y.numel() * 4)
+                gbs = byts / (ms * 1e-3) / 1e9
+                dq.append({"bits": bits, "tokens": n, "scales": str(sc.dtype).split(".")[-1],
+                           "ms": round(ms, 4), "bytes": byts, "GB/s": round(gbs, 1),
+                           "frac_hbm": round(gbs / PEAK_HBM_GBS, 4)})
+        del qw, sc32, zp
+    out["dequant_matmul"] = {"shape": f"{m}x{d} g{g}, bf16 activations, fp32 out",
+                             "bound": "hbm", "peak_GB/s": PEAK_HBM_GBS, "runs": dq}
+    torch.cuda.empty_cache()
+    # ---- quantizer variants on the attention-projection layer (S given)
+    L = synth.attn_proj_layer(dev)
+    W, X = L["W"], L["X"]
+    n_tok = X.shape[0]
+    S = torch.zeros(W.shape[1], W.shape[1], device=dev)
+    gq.gptq_hessian_accumulate(S, X)
+    base = dict(L["params"])
+    var = {}
+    for name, extra in (("minmax g128 (metric)", {}), ("symmetric g128", {"grid": "symmetric"}),
+                        ("static g128 act-order", {"static_groups": True, "act_order": True}),
+                        ("ternary g8", {"grid": "symmetric", "bits": 2, "group_size": 8}),
+                        ("8-bit row", {"bits": 8, "group_size": -1})):
+        p = dict(base, **extra)
+        var[name] = round(_event_ms(torch, lambda: gq.gptq_quantize_layer(W, S, n_tok, **p), 3), 3)
+    out["variants_quantize_ms"] = {"workload": "4096x4096, S of 262144 tokens given", **var}
+    # ---- layer-by-layer driver: four 4096 x 4096 layers, ReLU between
+    Ws = [W] + [synth.normal_weight(4096, 4096, 0.02, 8, f"stack/{i}", dev) for i in range(3)]
+    Xs = X[:65536].contiguous()
+    ms = _event_ms(torch, lambda: gq.gptq_quantize_stack(Ws, Xs, base, "relu"), 2)
+    out["stack_driver"] = {"workload": "4 layers 4096x4096, 65536 tokens, 4-bit g128, ReLU",
+                           "ms": round(ms, 3), "ms_per_layer": round(ms / 4, 3)}
+    return out
+
+
 def phase_rooflines(ph, m, d, N, bits, gsize, bsize):
     """Per-phase achieved rates against the published peaks, from the
     library's per-phase event tracing (milliseconds per layer)."""
@@ -385,6 +460,7 @@ def main():
         del L, W, X
         torch.cuda.empty_cache()
         line["workloads"] = workloads(gq, torch, synth, names, dev)
+        line["next_rows"] = next_rows(gq, torch, synth, dev)
         W, X = Wc, Xc
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(W, X, params, N, args.cpu_tokens, args.cpu_rows)

@@ -59,7 +59,7 @@ typedef enum gptq_status {
   GPTQ_ERR_HIP = 4          /* a HIP launch or runtime call failed              */
 } gptq_status;
 
-typedef enum gptq_dtype { GPTQ_BF16 = 0, GPTQ_F32 = 1 } gptq_dtype;
+typedef enum gptq_dtype { GPTQ_BF16 = 0, GPTQ_F32 = 1, GPTQ_F16 = 2 } gptq_dtype;
 
 /* The quantization grid ([derivation] 1.1 fit, eq. (36) encoder). */
 typedef enum gptq_grid {
@@ -232,17 +232,21 @@ gptq_status gptq_quantize_layer(const void* W, gptq_dtype w_dtype, int64_t m,
  *
  * X: bf16 activations [n, d] token-major, row stride ldx >= d (GPTQ_BF16
  *    only); 0 <= n <= 524280 (tiles of up to 8 rows share one weight pass).
- * qweight, scales, zeros, g_idx: exactly as gptq_quantize_layer writes them
- *    (qweight [m, ceil(d*bits/32)] uint32, scales fp32 / zeros uint8
- *    [m, n_g] with n_g from group_size, g_idx int32 [d], values < n_g).
+ * qweight, scales, zeros, g_idx: as gptq_quantize_layer writes them
+ *    (qweight [m, ceil(d*bits/32)] uint32, scales / zeros uint8 [m, n_g]
+ *    with n_g from group_size, g_idx int32 [d], values < n_g).
+ * scale_dtype: GPTQ_F32 (the scales as written) or GPTQ_F16 (the compact
+ *    16-bit storage of the steps: fp16 scales [m, n_g], e.g. the fp32 ones
+ *    rounded to nearest; each is widened exactly to fp32 in the kernel).
  * Y: fp32 [n, m], row stride ldy >= m; fully overwritten.
  * Sums in fp32 (each group's grid factored out of its 8-column runs).
- * Errors: INVALID_ARG (bad sizes, dtype, bits, group_size, NULL pointers
- *         when n > 0); HIP.  Allocates nothing; no workspace.
+ * Errors: INVALID_ARG (bad sizes, dtype, scale_dtype, bits, group_size,
+ *         NULL pointers when n > 0); HIP.  Allocates nothing; no workspace.
  * ------------------------------------------------------------------------- */
 gptq_status gptq_dequant_matmul(const void* X, gptq_dtype x_dtype, int64_t n,
                                 int64_t d, int64_t ldx, const uint32_t* qweight,
-                                const float* scales, const uint8_t* zeros,
+                                const void* scales, gptq_dtype scale_dtype,
+                                const uint8_t* zeros,
                                 const int32_t* g_idx, int64_t m, int32_t bits,
                                 int32_t group_size, int32_t signed_codes,
                                 float* Y, int64_t ldy, void* stream);

@@ -25,7 +25,7 @@ __all__ = [
 ]
 
 GPTQ_OK, GPTQ_ERR_INVALID_ARG, GPTQ_ERR_NOT_SPD, GPTQ_ERR_WORKSPACE, GPTQ_ERR_HIP = range(5)
-GPTQ_BF16, GPTQ_F32 = 0, 1
+GPTQ_BF16, GPTQ_F32, GPTQ_F16 = 0, 1, 2
 GPTQ_NOALLOC_SCRATCH_BYTES = 256 << 20      # include/gptq.h
 
 EXPORTED_SYMBOLS = (
@@ -94,8 +94,8 @@ def load_library():
     lib.gptq_hessian_accumulate_noalloc.restype = ctypes.c_int
     lib.gptq_hessian_accumulate_noalloc.argtypes = [vp, i64, vp, ctypes.c_int, i64, i64, vp]
     lib.gptq_dequant_matmul.restype = ctypes.c_int
-    lib.gptq_dequant_matmul.argtypes = [vp, ctypes.c_int, i64, i64, i64, vp, vp, vp, vp,
-                                        i64, i32, i32, i32, vp, i64, vp]
+    lib.gptq_dequant_matmul.argtypes = [vp, ctypes.c_int, i64, i64, i64, vp, vp, ctypes.c_int,
+                                        vp, vp, i64, i32, i32, i32, vp, i64, vp]
     sp = ctypes.POINTER(_StackLayer)
     lib.gptq_stack_workspace_bytes.restype = sz
     lib.gptq_stack_workspace_bytes.argtypes = [sp, i32, i64]
@@ -340,7 +340,8 @@ def gptq_dequant_matmul(X: torch.Tensor, qweight: torch.Tensor, scales: torch.Te
                         zeros: torch.Tensor, g_idx: torch.Tensor, bits: int,
                         group_size: int, signed: bool = False, Y=None) -> torch.Tensor:
     """Y [n, m] fp32 = X W_hat^T for bf16 activations X [n, d] and the stored
-    format of gptq_quantize_layer (qweight, scales, zeros, g_idx)."""
+    format of gptq_quantize_layer (qweight, scales, zeros, g_idx); scales
+    may be float32 or the compact float16 storage."""
     if X.dim() != 2:
         raise ValueError("X must be [n, d]")
     n, d = X.shape
@@ -355,7 +356,9 @@ def gptq_dequant_matmul(X: torch.Tensor, qweight: torch.Tensor, scales: torch.Te
         raise TypeError("qweight must be int32/uint32")
     if tuple(qweight.shape) != (m, words) or not qweight.is_contiguous():
         raise ValueError(f"qweight must be contiguous [{m}, {words}]")
-    _expect(scales, "scales", torch.float32, (m, ng), dev)
+    if scales.dtype not in (torch.float32, torch.float16):
+        raise TypeError("scales must be float32 or float16")
+    _expect(scales, "scales", scales.dtype, (m, ng), dev)
     _expect(zeros, "zeros", torch.uint8, (m, ng), dev)
     _expect(g_idx, "g_idx", torch.int32, (d,), dev)
     if qweight.device != dev:
@@ -364,8 +367,9 @@ def gptq_dequant_matmul(X: torch.Tensor, qweight: torch.Tensor, scales: torch.Te
         Y = torch.empty(n, m, dtype=torch.float32, device=dev)
     else:
         _expect(Y, "Y", torch.float32, (n, m), dev)
+    sdt = GPTQ_F16 if scales.dtype == torch.float16 else GPTQ_F32
     st = _lib().gptq_dequant_matmul(_dev_ptr(X), GPTQ_BF16, n, d, ldx, _dev_ptr(qweight),
-                                    _dev_ptr(scales), _dev_ptr(zeros), _dev_ptr(g_idx),
+                                    _dev_ptr(scales), sdt, _dev_ptr(zeros), _dev_ptr(g_idx),
                                     m, int(bits), int(group_size), int(bool(signed)),
                                     _dev_ptr(Y), m, _stream(dev))
     _check(st, "gptq_dequant_matmul")

@@ -160,7 +160,7 @@ gptq_status launch_outputs(int64_t m, int64_t d, int bits, int gsize, int sgn,
 // activation act (0 none, 1 ReLU, 2 SiLU).  n <= 524280.
 gptq_status launch_dequant_matmul(const uint16_t* X, int64_t ldx, int64_t n,
                                   const uint32_t* qweight, int64_t m, int64_t d,
-                                  int bits, const float* scales,
+                                  int bits, const void* scales, int scale_f16,
                                   const uint8_t* zeros, int64_t ng,
                                   const int32_t* g_idx, int sgn, void* Y,
                                   int64_t ldy, int out_bf16, int act,

@@ -385,11 +385,13 @@ gptq_status gptq_hessian_accumulate_noalloc(float* S, int64_t d, const void* X,
 
 gptq_status gptq_dequant_matmul(const void* X, gptq_dtype x_dtype, int64_t n,
                                 int64_t d, int64_t ldx, const uint32_t* qweight,
-                                const float* scales, const uint8_t* zeros,
+                                const void* scales, gptq_dtype scale_dtype,
+                                const uint8_t* zeros,
                                 const int32_t* g_idx, int64_t m, int32_t bits,
                                 int32_t group_size, int32_t signed_codes,
                                 float* Y, int64_t ldy, void* stream) {
-  if (x_dtype != GPTQ_BF16 || n < 0 || d <= 0 || m <= 0 || d > kMaxDim ||
+  if (x_dtype != GPTQ_BF16 || (scale_dtype != GPTQ_F32 && scale_dtype != GPTQ_F16) ||
+      n < 0 || d <= 0 || m <= 0 || d > kMaxDim ||
       ldx < d || ldy < m || !(bits == 2 || bits == 3 || bits == 4 || bits == 8) ||
       !(group_size == -1 || group_size > 0) ||
       (signed_codes != 0 && signed_codes != 1))
@@ -399,8 +401,8 @@ gptq_status gptq_dequant_matmul(const void* X, gptq_dtype x_dtype, int64_t n,
   const int64_t ng = group_size > 0 ? (d + group_size - 1) / group_size : 1;
   if (n > int64_t(65535) * 8) return GPTQ_ERR_INVALID_ARG;
   return launch_dequant_matmul(static_cast<const uint16_t*>(X), ldx, n, qweight, m,
-                               d, bits, scales, zeros, ng, g_idx, signed_codes, Y,
-                               ldy, 0, 0, static_cast<hipStream_t>(stream));
+                               d, bits, scales, scale_dtype == GPTQ_F16, zeros, ng, g_idx,
+                               signed_codes, Y, ldy, 0, 0, static_cast<hipStream_t>(stream));
 }
 
 size_t gptq_stack_workspace_bytes(const gptq_stack_layer* layers, int32_t n_layers,
@@ -445,7 +447,7 @@ gptq_status gptq_quantize_stack(const gptq_stack_layer* layers, int32_t n_layers
       return s;
     const int64_t ng = a.params.group_size > 0 ? (a.d + a.params.group_size - 1) / a.params.group_size : 1;
     if ((s = launch_dequant_matmul(static_cast<const uint16_t*>(Xc), a.d, n_tok, a.qweight,
-                                   a.m, a.d, a.params.bits, a.scales, a.zeros, ng, a.g_idx,
+                                   a.m, a.d, a.params.bits, a.scales, 0, a.zeros, ng, a.g_idx,
                                    a.params.grid == GPTQ_GRID_SYMMETRIC, Xn, a.m, 1,
                                    activation, st)) != GPTQ_OK)
       return s;

@@ -62,11 +62,18 @@ __device__ inline float activate(float v, int act) {
 }
 
 // out_bf16 = 0: Y fp32; 1: Y bf16 after the activation `act`.
-template <int BITS, int NX>
+// Step Delta of (row, group) index i: fp32, or fp16 widened exactly.
+template <bool SF16>
+__device__ inline float load_scale(const void* __restrict__ p, int64_t i) {
+  if (SF16) return static_cast<float>(static_cast<const _Float16*>(p)[i]);
+  return static_cast<const float*>(p)[i];
+}
+
+template <int BITS, int NX, bool SF16>
 __global__ __launch_bounds__(256) void dequant_matmul_kernel(
     const uint16_t* __restrict__ X, int64_t ldx, int64_t n,
     const uint32_t* __restrict__ qw, int64_t words,
-    const float* __restrict__ scales, const uint8_t* __restrict__ zeros,
+    const void* __restrict__ scales, const uint8_t* __restrict__ zeros,
     int64_t ng, const int32_t* __restrict__ g_idx, int64_t m, int64_t d,
     int sgn, void* __restrict__ Y, int64_t ldy, int out_bf16, int act) {
   __shared__ __attribute__((aligned(16))) uint16_t xs[NX][kChunk];
@@ -151,7 +158,7 @@ __global__ __launch_bounds__(256) void dequant_matmul_kernel(
           }
 #pragma unroll
           for (int r = 0; r < kRowsPerWave; ++r) {
-            const float s = scales[rows[r] * ng + G];
+            const float s = load_scale<SF16>(scales, rows[r] * ng + G);
             const float z = static_cast<float>(zeros[rows[r] * ng + G]);
             float cv[8];
 #pragma unroll
@@ -174,7 +181,7 @@ __global__ __launch_bounds__(256) void dequant_matmul_kernel(
             const int Gi = gs[cl + i];
 #pragma unroll
             for (int r = 0; r < kRowsPerWave; ++r) {
-              const float s = scales[rows[r] * ng + Gi];
+              const float s = load_scale<SF16>(scales, rows[r] * ng + Gi);
               const float z = static_cast<float>(zeros[rows[r] * ng + Gi]);
               const uint32_t c = code_at<BITS>(w[r], sb, i);
               const float cv = sgn ? static_cast<float>(static_cast<int>(c ^ hb) - static_cast<int>(hb))
@@ -216,16 +223,16 @@ __global__ __launch_bounds__(256) void dequant_matmul_kernel(
 
 unsigned cdiv(int64_t a, int64_t b) { return static_cast<unsigned>((a + b - 1) / b); }
 
-template <int BITS>
+template <int BITS, bool SF16>
 gptq_status launch_bits(const uint16_t* X, int64_t ldx, int64_t n, const uint32_t* qw,
-                        int64_t words, const float* scales, const uint8_t* zeros,
+                        int64_t words, const void* scales, const uint8_t* zeros,
                         int64_t ng, const int32_t* g_idx, int64_t m, int64_t d,
                         int sgn, void* Y, int64_t ldy, int out_bf16, int act,
                         hipStream_t st) {
   const int nx = n <= 1 ? 1 : n <= 4 ? 4 : 8;
   const dim3 grid(cdiv(m, kRowsPerWg), cdiv(n, nx));
 #define GPTQ_DQ(NXV)                                                                 \
-  dequant_matmul_kernel<BITS, NXV><<<grid, 256, 0, st>>>(X, ldx, n, qw, words, scales, \
+  dequant_matmul_kernel<BITS, NXV, SF16><<<grid, 256, 0, st>>>(X, ldx, n, qw, words, scales, \
                                                          zeros, ng, g_idx, m, d, sgn, Y, ldy, \
                                                          out_bf16, act)
   if (nx == 1)
@@ -243,7 +250,7 @@ gptq_status launch_bits(const uint16_t* X, int64_t ldx, int64_t n, const uint32_
 
 gptq_status launch_dequant_matmul(const uint16_t* X, int64_t ldx, int64_t n,
                                   const uint32_t* qweight, int64_t m, int64_t d,
-                                  int bits, const float* scales,
+                                  int bits, const void* scales, int scale_f16,
                                   const uint8_t* zeros, int64_t ng,
                                   const int32_t* g_idx, int sgn, void* Y,
                                   int64_t ldy, int out_bf16, int act,
@@ -251,8 +258,11 @@ gptq_status launch_dequant_matmul(const uint16_t* X, int64_t ldx, int64_t n,
   if (n == 0) return GPTQ_OK;
   if (n > int64_t(65535) * 8) return GPTQ_ERR_INVALID_ARG;   // grid.y
   const int64_t words = (d * bits + 31) / 32;
-#define GPTQ_DQB(B) \
-  launch_bits<B>(X, ldx, n, qweight, words, scales, zeros, ng, g_idx, m, d, sgn, Y, ldy, out_bf16, act, st)
+#define GPTQ_DQB(B)                                                                       \
+  (scale_f16 ? launch_bits<B, true>(X, ldx, n, qweight, words, scales, zeros, ng, g_idx, m, d, \
+                                    sgn, Y, ldy, out_bf16, act, st)                           \
+             : launch_bits<B, false>(X, ldx, n, qweight, words, scales, zeros, ng, g_idx, m, d, \
+                                     sgn, Y, ldy, out_bf16, act, st))
   switch (bits) {
     case 2: return GPTQ_DQB(2);
     case 3: return GPTQ_DQB(3);

@@ -34,7 +34,7 @@ namespace {
 constexpr int kNb = 64;          // diagonal block / panel width
 constexpr int kGroup = 4;        // blocks per trailing update (k = 256)
 constexpr int64_t kCUs = 256;     // MI355X compute units
-constexpr int64_t kBgTiles = 2;   // deferred trailing tiles per idle workgroup
+constexpr int64_t kBgTiles = 1;   // deferred trailing tiles per idle workgroup
 constexpr double kEpsFloor = 1.1920928955078125e-07;   // 2^-23
 
 // ---------------------------------------------------------------------------

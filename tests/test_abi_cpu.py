@@ -194,21 +194,23 @@ def test_binding_rejects_overlapping_rows_and_wrong_types():
 def test_dequant_matmul_rejects(lib):
     INV = gq.GPTQ_ERR_INVALID_ARG
     f = lib.gptq_dequant_matmul
-    ok = dict(X=FAKE, dt=0, n=4, d=64, ldx=64, qw=FAKE, sc=FAKE, zp=FAKE, gi=FAKE,
+    ok = dict(X=FAKE, dt=0, n=4, d=64, ldx=64, qw=FAKE, sc=FAKE, sdt=1, zp=FAKE, gi=FAKE,
               m=32, bits=4, g=32, sgn=0, Y=FAKE, ldy=32)
 
     def call(**kw):
         a = dict(ok, **kw)
-        return f(a["X"], a["dt"], a["n"], a["d"], a["ldx"], a["qw"], a["sc"], a["zp"],
-                 a["gi"], a["m"], a["bits"], a["g"], a["sgn"], a["Y"], a["ldy"], None)
+        return f(a["X"], a["dt"], a["n"], a["d"], a["ldx"], a["qw"], a["sc"], a["sdt"],
+                 a["zp"], a["gi"], a["m"], a["bits"], a["g"], a["sgn"], a["Y"], a["ldy"], None)
 
-    for kw in (dict(dt=1), dict(n=-1), dict(d=0), dict(m=0), dict(ldx=63), dict(ldy=31),
+    for kw in (dict(dt=1), dict(dt=2), dict(sdt=0), dict(sdt=3), dict(n=-1), dict(d=0),
+               dict(m=0), dict(ldx=63), dict(ldy=31),
                dict(bits=5), dict(g=0), dict(g=-2), dict(sgn=2), dict(X=None),
                dict(qw=None), dict(sc=None), dict(zp=None), dict(gi=None), dict(Y=None),
                dict(d=70000, ldx=70000)):
         assert call(**kw) == INV, kw
-    # n = 0 launches nothing and succeeds without a GPU
+    # n = 0 launches nothing and succeeds without a GPU (fp32 or fp16 scales)
     assert call(n=0, X=None, Y=None) == gq.GPTQ_OK
+    assert call(n=0, X=None, Y=None, sdt=2) == gq.GPTQ_OK
 
 
 def test_stack_rejects(lib):

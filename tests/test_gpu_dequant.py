@@ -4,7 +4,8 @@ weights dequantized inside the matmul; format of [derivation] 3.1 / 8.3).
 
 Stored formats come from the oracle (gptq_layer on seeded synthetic layers:
 dynamic groups with act-order, static groups, whole-row grids, signed
-symmetric codes) and from seeded random codes; activations are bf16.
+symmetric codes) and from seeded random codes; activations are bf16; the
+steps fp32, or fp16 (the compact storage).
 
 Tolerance from the arithmetic: the kernel forms, per 8-column run sharing
 one grid, Delta (sum x c - z sum x), and adds the runs in an fp32 running
@@ -32,16 +33,21 @@ def dev():
     return torch.device("cuda:0")
 
 
-def _check(dev, X, packed, scales, zeros, g_idx, bits, group_size, signed, m):
+def _check(dev, X, packed, scales, zeros, g_idx, bits, group_size, signed, m, f16=False):
+    """f16: the scales stored as fp16 (rounded to nearest from the given
+    ones); the oracle then takes the same rounded steps."""
     d = X.shape[1]
+    if f16:
+        scales = np.asarray(scales, dtype=np.float32).astype(np.float16)
     Y = gq.gptq_dequant_matmul(
         X.to(dev), torch.from_numpy(packed.view(np.int32)).to(dev),
-        torch.from_numpy(np.asarray(scales, dtype=np.float32)).to(dev),
+        torch.from_numpy(np.asarray(scales, dtype=np.float16 if f16 else np.float32)).to(dev),
         torch.from_numpy(np.asarray(zeros, dtype=np.uint8)).to(dev),
         torch.from_numpy(np.asarray(g_idx, dtype=np.int32)).to(dev),
         bits, group_size, signed)
     torch.cuda.synchronize()
     x64 = X.double().numpy()
+    scales = np.asarray(scales, dtype=np.float64)
     Y_o = orc.dequant_matmul(x64, packed, scales, zeros, g_idx, bits, signed)
     codes = orc.unpack_codes(packed, d, bits)
     if signed:
@@ -97,6 +103,23 @@ def test_dequant_matmul_random_codes(dev, bits):
     X = synth.lowrank_outlier_acts(d, 5, 53, f"dq/R/{bits}", "cpu")
     _check(dev, X, packed, scales, zeros, g_idx, bits, g, False, m)
     _check(dev, X, packed, scales, np.zeros_like(zeros), g_idx, bits, g, True, m)
+
+
+@pytest.mark.parametrize("case", LAYERS[:4], ids=lambda c: "m{m}_d{d}_b{bits}_g{group_size}".format(**c))
+def test_dequant_matmul_fp16_scales(dev, case):
+    """The compact storage of the steps: fp16 scales, widened exactly in the
+    kernel; against the oracle's product on the same rounded steps."""
+    c = dict(case)
+    m, d = c.pop("m"), c.pop("d")
+    W = synth.normal_weight(m, d, 0.02, 51, f"dq/W/{m}/{d}", "cpu")
+    Xc = synth.decaying_spectrum_acts(d, 600, 51, f"dq/X/{d}", "cpu")
+    S = orc.hessian_sum(Xc.double().numpy())
+    res = orc.gptq_layer(W.double().numpy(), S, 600, blocksize=128, **c)
+    zeros = np.zeros_like(res.zeros) if res.signed else res.zeros
+    for n in (1, 8, 13):
+        X = synth.lowrank_outlier_acts(d, n, 54, f"dq/H/{d}/{n}", "cpu")
+        _check(dev, X, res.packed, res.scales, zeros, res.g_idx, c["bits"],
+               c["group_size"], res.signed, m, f16=True)
 
 
 def test_dequant_matmul_empty_batch(dev):

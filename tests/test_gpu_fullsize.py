@@ -9,8 +9,9 @@ What the oracle affords at these sizes:
     the layer along two routes (see independent_layer): the oracle's loop on
     the GPU's S (gating) and the oracle's own S, factor and loop from X,
     fully independent of the GPU, with an oracle-against-itself control.
-    The benchmarked attention projection compares every row; the others a
-    seeded sample of 1024-2048 rows unless GPTQ_FULLSIZE_ALL_ROWS=1.
+    A seeded sample of 512-1024 rows per layer by default (the whole file
+    then runs in about a quarter of an hour); every row with
+    GPTQ_FULLSIZE_ALL_ROWS=1.
   * d = 11008 and 12288 (MLP down, decoder-block down, d_model-12288 W and
     fc1): the float64 S over 262144 tokens is out of the host's reach, so S
     is checked on a sampled block of exact float64 dot products, and the
@@ -45,10 +46,10 @@ from parity import compare_layer
 
 pytestmark = pytest.mark.gpu
 
-# Every output row through the oracle on every layer when set; otherwise
-# the layers other than the benchmarked one compare a seeded sample of rows
-# (rows are independent given R and their grids, [derivation] 2.3), which
-# keeps this file's run within a quarter of an hour of host time.
+# Every output row through the oracle on every d = 4096 layer when set;
+# otherwise a seeded sample of rows (rows are independent given R and their
+# grids, [derivation] 2.3), which keeps this file's run within about a
+# quarter of an hour of host time.
 ALL_ROWS = os.environ.get("GPTQ_FULLSIZE_ALL_ROWS", "") == "1"
 
 
@@ -437,17 +438,18 @@ def stagewise_layer(tag, W, X, params, rng, nrows=None, S=None, factor=None,
 
 
 def test_attention_projection_full(dev):
-    """The benchmarked layer: 4096 x 4096, 262144 tokens, 4-bit g128; every
-    row against the fully independent oracle."""
+    """The benchmarked layer: 4096 x 4096, 262144 tokens, 4-bit g128; the
+    fully independent oracle gates as well (every row with
+    GPTQ_FULLSIZE_ALL_ROWS=1)."""
     L = synth.attn_proj_layer(dev)
-    independent_layer("attn_proj", L["W"], L["X"], L["params"])
+    independent_layer("attn_proj", L["W"], L["X"], L["params"], nrows=1024, seed=20)
 
 
 def test_mlp_up_full(dev):
     """Up 11008 x 4096, 3-bit g128, act-order; every row, independent."""
     P = synth.mlp_pair(dev)
     independent_layer("mlp_up", P["up"]["W"], P["up"]["X"], P["up"]["params"],
-                      gate_from_x=False, nrows=2048, seed=21)
+                      gate_from_x=False, nrows=1024, seed=21)
 
 
 def test_mlp_down_full(dev):
@@ -455,7 +457,7 @@ def test_mlp_down_full(dev):
     P = synth.mlp_pair(dev)
     del P["up"]
     stagewise_layer("mlp_down", P["down"]["W"], P["down"]["X"], P["down"]["params"],
-                    np.random.default_rng(12), nrows=1024)
+                    np.random.default_rng(12), nrows=512)
 
 
 def test_decoder_block_qkv_full(dev):
@@ -470,37 +472,43 @@ def test_decoder_block_qkv_full(dev):
     cache = {}
     for i, nm in enumerate(("q", "k", "v")):
         independent_layer(f"block_{nm}", B[nm]["W"], X, p, S=S, factor=(Rt, pt, dt),
-                          cache=cache, gate_from_x=False, nrows=1024, seed=30 + i)
+                          cache=cache, gate_from_x=False, nrows=512, seed=30 + i)
 
 
 def test_decoder_block_o_full(dev):
     """o (4096 x 4096) on the attention output; every row, both routes."""
     B = synth.decoder_block(dev)
     independent_layer("block_o", B["o"]["W"], B["o"]["X"], B["o"]["params"],
-                      gate_from_x=False, nrows=1024, seed=33)
+                      gate_from_x=False, nrows=512, seed=33)
 
 
-def test_decoder_block_gate_up_full(dev):
-    """gate and up (11008 x 4096) on one shared factor: every row on the
-    same S, the first 4096 rows also from X with the control."""
+def _gate_up(dev, name, seed):
+    """gate or up (11008 x 4096) on the factor both share (computed once
+    from their common input and passed in): the rows on the same S, the
+    first 4096 of them also from X with the control."""
     B = synth.decoder_block(dev)
     p = B["gate"]["params"]
     X = B["gate"]["X"]
     n = X.shape[0]
     S = accumulate(X)
     Rt, pt, dt, _ = gq.gptq_cholesky_inverse(S, n, p["percdamp"], p["act_order"])
-    cache = {}
-    for i, nm in enumerate(("gate", "up")):
-        independent_layer(f"block_{nm}", B[nm]["W"], X, p, S=S, factor=(Rt, pt, dt),
-                          cache=cache, gate_from_x=False, from_x_rows=4096,
-                          nrows=1024, seed=34 + i)
+    independent_layer(f"block_{name}", B[name]["W"], X, p, S=S, factor=(Rt, pt, dt),
+                      gate_from_x=False, from_x_rows=4096, nrows=512, seed=seed)
+
+
+def test_decoder_block_gate_full(dev):
+    _gate_up(dev, "gate", 34)
+
+
+def test_decoder_block_up_full(dev):
+    _gate_up(dev, "up", 35)
 
 
 def test_decoder_block_down_full(dev):
     """down (4096 x 11008) on the SiLU-gated input, 1024 sampled rows."""
     B = synth.decoder_block(dev)
     stagewise_layer("block_down", B["down"]["W"], B["down"]["X"], B["down"]["params"],
-                    np.random.default_rng(13), nrows=1024)
+                    np.random.default_rng(13), nrows=512)
 
 
 def test_large_model_attn_full(dev):
