@@ -9,8 +9,9 @@ What the oracle affords at these sizes:
     the layer along two routes (see independent_layer): the oracle's loop on
     the GPU's S (gating) and the oracle's own S, factor and loop from X,
     fully independent of the GPU, with an oracle-against-itself control.
-    A seeded sample of 512-1024 rows per layer by default (the whole file
-    then runs in about a quarter of an hour); every row with
+    The benchmarked attention projection compares every row; the other
+    layers a seeded sample of 512-1024 rows by default (the whole file then
+    runs in about a quarter of an hour), every row with
     GPTQ_FULLSIZE_ALL_ROWS=1.
   * d = 11008 and 12288 (MLP down, decoder-block down, d_model-12288 W and
     fc1): the float64 S over 262144 tokens is out of the host's reach, so S
@@ -33,6 +34,7 @@ from __future__ import annotations
 import json
 import math
 import os
+import sys
 
 import numpy as np
 import pytest
@@ -51,6 +53,12 @@ pytestmark = pytest.mark.gpu
 # grids, [derivation] 2.3), which keeps this file's run within about a
 # quarter of an hour of host time.
 ALL_ROWS = os.environ.get("GPTQ_FULLSIZE_ALL_ROWS", "") == "1"
+
+
+def say(msg):
+    """Progress line on the process's own stderr (left alone by pytest's
+    output capture), so that a long comparison is seen to progress."""
+    print(msg, file=sys.__stderr__, flush=True)
 
 
 def row_sample(m, nrows, seed):
@@ -88,7 +96,7 @@ def oracle_S(X):
     S = np.zeros((d, d))
     for t0 in range(0, n, 16384):
         S += orc.hessian_sum(X[t0:t0 + 16384].cpu().to(torch.float64).numpy())
-        print(f"oracle S: {min(t0 + 16384, n)}/{n} tokens", flush=True)
+        say(f"oracle S: {min(t0 + 16384, n)}/{n} tokens")
     return S
 
 
@@ -329,12 +337,12 @@ def compare_rows(out, W, n, params, routes, rows=None, batch=1024, tag="",
             _agg_add(tot["control"], rep)
         msg = ", ".join(f"{k}: diverged {v['rows_diverged']} forced {v['forced']}"
                         for k, v in tot.items())
-        print(f"{tag}: rows {b0 + len(rb)}/{len(rows)} compared ({msg})", flush=True)
+        say(f"{tag}: rows {b0 + len(rb)}/{len(rows)} compared ({msg})")
     return {k: _agg_end(v, d) for k, v in tot.items()}
 
 
 def record(tag, **kw):
-    print("FULLSIZE " + json.dumps(dict(layer=tag, **kw)), flush=True)
+    say("FULLSIZE " + json.dumps(dict(layer=tag, **kw)))
 
 
 def independent_layer(tag, W, X, params, S=None, factor=None, cache=None,
@@ -360,7 +368,7 @@ def independent_layer(tag, W, X, params, S=None, factor=None, cache=None,
     if "S_o" not in cache:
         S_o = oracle_S(X)
         cache["s_err"] = check_S_full(S, S_o, n)
-        print(f"{tag}: S checked ({cache['s_err']:.2e})", flush=True)
+        say(f"{tag}: S checked ({cache['s_err']:.2e})")
         R, perm, dead, damp = gq.gptq_cholesky_inverse(S, n, params["percdamp"],
                                                        params["act_order"])
         # the factor's own precision: the oracle's factor of the GPU's S
@@ -372,7 +380,7 @@ def independent_layer(tag, W, X, params, S=None, factor=None, cache=None,
         assert math.isclose(damp, damp_g, rel_tol=1e-6), (damp, damp_g)
         R_g, _ = orc.factor(H, damp_g)
         cache["r_err"] = check_R_entrywise(R, R_g)
-        print(f"{tag}: R checked {cache['r_err']}", flush=True)
+        say(f"{tag}: R checked {cache['r_err']}")
         del H, R
         perm_o, dead_o, R_o, swaps = oracle_factor_tie_forced(S_o, n, params, perm_g)
         cache.update(S_o=S_o, S64=S64, R_o=R_o, perm_o=perm_o, dead_o=dead_o,
@@ -406,10 +414,10 @@ def stagewise_layer(tag, W, X, params, rng, nrows=None, S=None, factor=None,
     n, d = X.shape
     S = accumulate(X) if S is None else S
     s_info = check_S_sampled(S, X, rng)
-    print(f"{tag}: S sampled {s_info}", flush=True)
+    say(f"{tag}: S sampled {s_info}")
     R, perm, dead, damp = gq.gptq_cholesky_inverse(S, n, params["percdamp"], params["act_order"])
     ident = check_R_identity(R, S, n, perm, dead, damp, rng)
-    print(f"{tag}: R H R^T = I to {ident:.2e}", flush=True)
+    say(f"{tag}: R H R^T = I to {ident:.2e}")
     perm_np = perm.cpu().numpy()
     dead_np = dead.cpu().numpy().astype(bool)
     S64 = np64(S)
@@ -421,7 +429,7 @@ def stagewise_layer(tag, W, X, params, rng, nrows=None, S=None, factor=None,
         R_o, _ = orc.factor(H, damp_g)
         del H
         r_ent, r_fro = check_R_entrywise(R, R_o)
-        print(f"{tag}: R checked {r_ent:.2e} {r_fro:.2e}", flush=True)
+        say(f"{tag}: R checked {r_ent:.2e} {r_fro:.2e}")
     else:
         # too large for the host factor: the loop runs on the GPU's R, which
         # the identity above checks
@@ -438,11 +446,10 @@ def stagewise_layer(tag, W, X, params, rng, nrows=None, S=None, factor=None,
 
 
 def test_attention_projection_full(dev):
-    """The benchmarked layer: 4096 x 4096, 262144 tokens, 4-bit g128; the
-    fully independent oracle gates as well (every row with
-    GPTQ_FULLSIZE_ALL_ROWS=1)."""
+    """The benchmarked layer: 4096 x 4096, 262144 tokens, 4-bit g128; every
+    row, and the fully independent oracle gates as well."""
     L = synth.attn_proj_layer(dev)
-    independent_layer("attn_proj", L["W"], L["X"], L["params"], nrows=1024, seed=20)
+    independent_layer("attn_proj", L["W"], L["X"], L["params"])
 
 
 def test_mlp_up_full(dev):
