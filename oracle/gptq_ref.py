@@ -14,11 +14,13 @@ reading independently; "parity unpinned" = no page fixes a value for it):
   * H scale: H = (2/N) X X^T ([derivation] eq. (9)).  The toy example of
     [teardown] uses 2 X X^T; the helpers for it take H directly.
   * Rounding: round half to even (numpy ``rint``).            parity unpinned
-  * Grid fit (min-max, [derivation] section 1.1): the range is widened to
-    contain 0 so the zero point represents 0 exactly; an all-zero range is
-    replaced by [-1, 1]; Delta = (hi - lo) / (2^b - 1), z = rint(-lo/Delta).
-    The fit is evaluated in float32, the precision the scales are stored and
-    the kernel decides the integer zero point in.              parity unpinned
+  * Grid fit (min-max, [derivation] section 1.1): Delta = (hi - lo) /
+    (2^b - 1), z = rint(-lo / Delta) (pinned: a range whose -lo/Delta has a
+    fractional part above 1/2).  Our readings on top: the range is widened
+    to contain 0 so the zero point represents 0 exactly; an all-zero range
+    is replaced by [-1, 1]; the fit is evaluated in float32, the precision
+    the scales are stored and the kernel decides the integer zero point
+    in.                                                         parity unpinned
   * group_size = -1: one grid per row, fitted once on the ORIGINAL row before
     dead columns are zeroed ([derivation] section 10 pseudocode order).
   * group_size > 0: dynamic groups -- refitted at each group start, in

@@ -10,19 +10,21 @@
 // The weight stream is the HBM cost (b/8 bytes per weight); activations are
 // bf16 token rows (the "A16" of W4A16), products and sums fp32.
 //
-// Layout of the work: a workgroup owns 16 output rows (four per wave) and
-// one tile of up to NX activation rows; it walks the input dimension in
-// chunks of 2048 columns.  Per chunk the activations and the group ids are
-// staged in LDS (each 8-column sub-block also gets its group id when its 8
+// Layout of the work: a workgroup owns 32 output rows (eight per wave) for
+// one activation row, or 16 rows (four per wave) for a tile of 4 or 8
+// activation rows; it walks the input dimension in chunks of 2048 columns.
+// Per chunk the activations and the group ids are staged in LDS with
+// 16-byte loads (each 8-column sub-block also gets its group id when its 8
 // columns share one group -- always, for contiguous groups of a multiple of
 // 8 -- else -1), and lane l of every wave takes the 32-column segment l of
 // the chunk: the segment's codes are bits words of every row (column c of a
 // row starts at bit c * bits, so a 32-column segment is exactly `bits` whole
-// words), read coalesced across the wave.  A sub-block with one group
-// factors the group's grid out: sum_i x_i Delta (c_i - z) = Delta (sum_i x_i
-// c_i - z sum_i x_i); a mixed sub-block (act-order with dynamic groups)
-// dequantizes column by column.  The wave's 64 partial sums per (row,
-// token) are reduced with lane shuffles at the end.
+// words), one wide load per row, coalesced across the wave.  A sub-block
+// with one group factors the group's grid out: sum_i x_i Delta (c_i - z) =
+// Delta (sum_i x_i c_i - z sum_i x_i), the grid loaded once per run of
+// sub-blocks in that group; a mixed sub-block (act-order with dynamic
+// groups) dequantizes column by column.  The wave's 64 partial sums per
+// (row, token) are reduced with lane shuffles at the end.
 #include "common.h"
 
 namespace gptq {
@@ -30,8 +32,15 @@ namespace {
 
 constexpr int kChunk = 2048;           // columns per LDS chunk
 constexpr int kSub = kChunk / 8;       // 8-column sub-blocks per chunk
-constexpr int kRowsPerWave = 4;
-constexpr int kRowsPerWg = 4 * kRowsPerWave;
+
+// Rows per wave: eight for one activation row (the chunk's staging is then
+// shared by 32 rows per workgroup), four for the tiles of 4 or 8.
+constexpr int rows_per_wave(int nx) { return nx == 1 ? 8 : 4; }
+
+// 16-byte (or 8-byte) accesses allowed: bit 0 activations (ldx % 8 == 0,
+// 16-byte aligned), bit 1 group ids (16-byte aligned), bit 2 code words
+// (row stride and base aligned to the segment's load size).
+constexpr int kVecX = 1, kVecG = 2, kVecW = 4;
 
 __device__ inline float bf16_to_f32(uint32_t u) { return __uint_as_float(u << 16); }
 
@@ -43,6 +52,15 @@ __device__ inline uint32_t code_at(const uint32_t* w, int sb, int i) {
   uint32_t v = w[wi] >> off;
   if (off + BITS > 32) v |= w[wi + 1] << (32 - off);
   return v & ((1u << BITS) - 1u);
+}
+
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+
+// sum a.lo b.lo + a.hi b.hi + c of two bf16 pairs, accumulated in fp32
+// (the bf16 products are exact in fp32)
+__device__ inline float dot2_bf16(uint32_t a, uint32_t b, float c) {
+  return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, a),
+                                         __builtin_bit_cast(bf16x2, b), c, false);
 }
 
 // bf16 round to nearest even (NaN stays a quiet NaN).
@@ -75,9 +93,11 @@ __global__ __launch_bounds__(256) void dequant_matmul_kernel(
     const uint32_t* __restrict__ qw, int64_t words,
     const void* __restrict__ scales, const uint8_t* __restrict__ zeros,
     int64_t ng, const int32_t* __restrict__ g_idx, int64_t m, int64_t d,
-    int sgn, void* __restrict__ Y, int64_t ldy, int out_bf16, int act) {
+    int sgn, void* __restrict__ Y, int64_t ldy, int out_bf16, int act, int vec) {
+  constexpr int kRowsPerWave = rows_per_wave(NX);
+  constexpr int kRowsPerWg = 4 * kRowsPerWave;
   __shared__ __attribute__((aligned(16))) uint16_t xs[NX][kChunk];
-  __shared__ int32_t gs[kChunk];
+  __shared__ __attribute__((aligned(16))) int32_t gs[kChunk];
   __shared__ int32_t ug[kSub];
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
   const int64_t r0 = int64_t(blockIdx.x) * kRowsPerWg + kRowsPerWave * wv;
@@ -99,19 +119,32 @@ __global__ __launch_bounds__(256) void dequant_matmul_kernel(
     //      8t .. 8t + 7 of the chunk)
     {
       const int64_t cb = c0 + 8 * tid;
+      const bool full = cb + 8 <= d;
 #pragma unroll
       for (int k = 0; k < NX; ++k) {
-        uint16_t v[8];
         const bool krow = k < nk;
         const uint16_t* src = X + (k0 + (krow ? k : 0)) * ldx;
+        if ((vec & kVecX) && full) {
+          const uint4 v = *reinterpret_cast<const uint4*>(src + cb);
+          *reinterpret_cast<uint4*>(&xs[k][8 * tid]) = krow ? v : uint4{0u, 0u, 0u, 0u};
+        } else {
+          uint16_t v[8];
 #pragma unroll
-        for (int i = 0; i < 8; ++i) v[i] = (krow && cb + i < d) ? src[cb + i] : uint16_t(0);
+          for (int i = 0; i < 8; ++i) v[i] = (krow && cb + i < d) ? src[cb + i] : uint16_t(0);
 #pragma unroll
-        for (int i = 0; i < 8; ++i) xs[k][8 * tid + i] = v[i];
+          for (int i = 0; i < 8; ++i) xs[k][8 * tid + i] = v[i];
+        }
       }
       int32_t g[8];
+      if ((vec & kVecG) && full) {
+        const int4 a = *reinterpret_cast<const int4*>(g_idx + cb);
+        const int4 b = *reinterpret_cast<const int4*>(g_idx + cb + 4);
+        g[0] = a.x; g[1] = a.y; g[2] = a.z; g[3] = a.w;
+        g[4] = b.x; g[5] = b.y; g[6] = b.z; g[7] = b.w;
+      } else {
 #pragma unroll
-      for (int i = 0; i < 8; ++i) g[i] = g_idx[min<int64_t>(cb + i, d - 1)];
+        for (int i = 0; i < 8; ++i) g[i] = g_idx[min<int64_t>(cb + i, d - 1)];
+      }
       bool same = true;
 #pragma unroll
       for (int i = 1; i < 8; ++i) same = same && (g[i] == g[0] || cb + i >= d);
@@ -124,22 +157,57 @@ __global__ __launch_bounds__(256) void dequant_matmul_kernel(
     const int64_t seg = c0 / 32 + lane;
     if (seg * 32 < d) {
       uint32_t w[kRowsPerWave][BITS];
+      if ((vec & kVecW) && BITS != 3 && (seg + 1) * BITS <= words) {
+        // the segment's BITS words in one (two at 8 bits) wide load per row
 #pragma unroll
-      for (int i = 0; i < kRowsPerWave; ++i)
+        for (int i = 0; i < kRowsPerWave; ++i) {
+          const uint32_t* p = qw + rows[i] * words + seg * BITS;
+          if (BITS == 2) {
+            const uint2 v = *reinterpret_cast<const uint2*>(p);
+            w[i][0] = v.x; w[i][1 % BITS] = v.y;
+          } else {
 #pragma unroll
-        for (int j = 0; j < BITS; ++j) {
-          const int64_t wi = seg * BITS + j;
-          w[i][j] = wi < words ? qw[rows[i] * words + wi] : 0u;
+            for (int h = 0; h < BITS / 4; ++h) {
+              const uint4 v = *reinterpret_cast<const uint4*>(p + 4 * h);
+              w[i][(4 * h) % BITS] = v.x; w[i][(4 * h + 1) % BITS] = v.y;
+              w[i][(4 * h + 2) % BITS] = v.z; w[i][(4 * h + 3) % BITS] = v.w;
+            }
+          }
         }
+      } else {
+#pragma unroll
+        for (int i = 0; i < kRowsPerWave; ++i)
+#pragma unroll
+          for (int j = 0; j < BITS; ++j) {
+            const int64_t wi = seg * BITS + j;
+            w[i][j] = wi < words ? qw[rows[i] * words + wi] : 0u;
+          }
+      }
+      // the grid of the previous uniform sub-block, reused while the group
+      // stays the same (a 32-column segment usually lies in one group)
+      int Gp = -1;
+      float sc[kRowsPerWave], zc[kRowsPerWave];
 #pragma unroll
       for (int sb = 0; sb < 4; ++sb) {
         const int cl = 32 * lane + 8 * sb;          // column within the chunk
         if (c0 + cl >= d) break;
         float xv[NX][8];
+        uint32_t xp[NX][4];     // bf16 pairs (x0, x2), (x4, x6), (x1, x3), (x5, x7)
 #pragma unroll
         for (int k = 0; k < NX; ++k) {
           const uint4 raw = *reinterpret_cast<const uint4*>(&xs[k][cl]);
           const uint32_t u[4] = {raw.x, raw.y, raw.z, raw.w};
+          if (BITS == 4) {
+            xp[k][0] = __builtin_amdgcn_perm(raw.y, raw.x, 0x05040100u);
+            xp[k][1] = __builtin_amdgcn_perm(raw.w, raw.z, 0x05040100u);
+            xp[k][2] = __builtin_amdgcn_perm(raw.y, raw.x, 0x07060302u);
+            xp[k][3] = __builtin_amdgcn_perm(raw.w, raw.z, 0x07060302u);
+          } else if (BITS == 2) {   // (x0, x4), (x1, x5), (x2, x6), (x3, x7)
+            xp[k][0] = __builtin_amdgcn_perm(raw.z, raw.x, 0x05040100u);
+            xp[k][1] = __builtin_amdgcn_perm(raw.z, raw.x, 0x07060302u);
+            xp[k][2] = __builtin_amdgcn_perm(raw.w, raw.y, 0x05040100u);
+            xp[k][3] = __builtin_amdgcn_perm(raw.w, raw.y, 0x07060302u);
+          }
 #pragma unroll
           for (int i = 0; i < 4; ++i) {
             xv[k][2 * i] = bf16_to_f32(u[i] & 0xFFFFu);
@@ -156,10 +224,70 @@ __global__ __launch_bounds__(256) void dequant_matmul_kernel(
             for (int i = 0; i < 8; ++i) t += xv[k][i];
             xsum[k] = t;
           }
+          if (G != Gp) {
+#pragma unroll
+            for (int r = 0; r < kRowsPerWave; ++r) {
+              sc[r] = load_scale<SF16>(scales, rows[r] * ng + G);
+              zc[r] = static_cast<float>(zeros[rows[r] * ng + G]);
+            }
+            Gp = G;
+          }
+          if (BITS == 4) {
+            // the sub-block's 8 codes are word sb of the segment; each code
+            // k becomes the bf16 value 8 + k / 2 (exponent of 8, k in
+            // mantissa bits 3..6), two per register, and meets the matching
+            // activation pair in one fp32-accumulating dot product:
+            // t = sum x (8 + k / 2), so sum x (k - z) = 2 t - (16 + z) sum x.
+            // Signed codes: k = c ^ 8 = c_s + 8, i.e. the same with z = 8.
+#pragma unroll
+            for (int r = 0; r < kRowsPerWave; ++r) {
+              const uint32_t wr = w[r][sb % BITS] ^ (sgn ? 0x88888888u : 0u);
+              const uint32_t lo = (wr << 3) & 0x78787878u;   // codes 0, 2, 4, 6
+              const uint32_t hi = (wr >> 1) & 0x78787878u;   // codes 1, 3, 5, 7
+              const uint32_t p02 = __builtin_amdgcn_perm(0x41414141u, lo, 0x04010400u);
+              const uint32_t p46 = __builtin_amdgcn_perm(0x41414141u, lo, 0x04030402u);
+              const uint32_t p13 = __builtin_amdgcn_perm(0x41414141u, hi, 0x04010400u);
+              const uint32_t p57 = __builtin_amdgcn_perm(0x41414141u, hi, 0x04030402u);
+              const float zo = 16.0f + (sgn ? 8.0f : zc[r]);
+#pragma unroll
+              for (int k = 0; k < NX; ++k) {
+                float t = dot2_bf16(p02, xp[k][0], 0.0f);
+                t = dot2_bf16(p46, xp[k][1], t);
+                t = dot2_bf16(p13, xp[k][2], t);
+                t = dot2_bf16(p57, xp[k][3], t);
+                acc[r][k] = fmaf(sc[r], fmaf(-zo, xsum[k], 2.0f * t), acc[r][k]);
+              }
+            }
+          } else if (BITS == 2) {
+            // the sub-block's 8 codes are half sb % 2 of word sb / 2; code j
+            // (bits 2j) goes to mantissa bits 3..4 of a bf16 8 + k / 2 as
+            // above, pairs (c0, c4), (c1, c5), (c2, c6), (c3, c7).  Signed
+            // codes: k = c ^ 2 = c_s + 2.
+#pragma unroll
+            for (int r = 0; r < kRowsPerWave; ++r) {
+              const uint32_t v = ((w[r][(sb / 2) % BITS] >> (16 * (sb % 2))) & 0xFFFFu) ^
+                                 (sgn ? 0xAAAAu : 0u);
+              const uint32_t t04 = (v << 3) & 0x1818u, t15 = (v << 1) & 0x1818u;
+              const uint32_t t26 = (v >> 1) & 0x1818u, t37 = (v >> 3) & 0x1818u;
+              const uint32_t p04 = __builtin_amdgcn_perm(0x41414141u, t04, 0x04010400u);
+              const uint32_t p15 = __builtin_amdgcn_perm(0x41414141u, t15, 0x04010400u);
+              const uint32_t p26 = __builtin_amdgcn_perm(0x41414141u, t26, 0x04010400u);
+              const uint32_t p37 = __builtin_amdgcn_perm(0x41414141u, t37, 0x04010400u);
+              const float zo = 16.0f + (sgn ? 2.0f : zc[r]);
+#pragma unroll
+              for (int k = 0; k < NX; ++k) {
+                float t = dot2_bf16(p04, xp[k][0], 0.0f);
+                t = dot2_bf16(p15, xp[k][1], t);
+                t = dot2_bf16(p26, xp[k][2], t);
+                t = dot2_bf16(p37, xp[k][3], t);
+                acc[r][k] = fmaf(sc[r], fmaf(-zo, xsum[k], 2.0f * t), acc[r][k]);
+              }
+            }
+          } else {
 #pragma unroll
           for (int r = 0; r < kRowsPerWave; ++r) {
-            const float s = load_scale<SF16>(scales, rows[r] * ng + G);
-            const float z = static_cast<float>(zeros[rows[r] * ng + G]);
+            const float s = sc[r];
+            const float z = zc[r];
             float cv[8];
 #pragma unroll
             for (int i = 0; i < 8; ++i) {
@@ -174,6 +302,7 @@ __global__ __launch_bounds__(256) void dequant_matmul_kernel(
               for (int i = 0; i < 8; ++i) t = fmaf(xv[k][i], cv[i], t);
               acc[r][k] = fmaf(s, fmaf(-z, xsum[k], t), acc[r][k]);
             }
+          }
           }
         } else {
 #pragma unroll
@@ -230,11 +359,17 @@ gptq_status launch_bits(const uint16_t* X, int64_t ldx, int64_t n, const uint32_
                         int sgn, void* Y, int64_t ldy, int out_bf16, int act,
                         hipStream_t st) {
   const int nx = n <= 1 ? 1 : n <= 4 ? 4 : 8;
-  const dim3 grid(cdiv(m, kRowsPerWg), cdiv(n, nx));
+  const int64_t rows_wg = 4 * rows_per_wave(nx);
+  const dim3 grid(cdiv(m, rows_wg), cdiv(n, nx));
+  const int wbytes = BITS == 2 ? 8 : 16;       // wide code load of one segment
+  const int vec = ((ldx % 8 == 0 && reinterpret_cast<uintptr_t>(X) % 16 == 0) ? kVecX : 0) |
+                  (reinterpret_cast<uintptr_t>(g_idx) % 16 == 0 ? kVecG : 0) |
+                  ((words * 4 % wbytes == 0 && reinterpret_cast<uintptr_t>(qw) % wbytes == 0)
+                       ? kVecW : 0);
 #define GPTQ_DQ(NXV)                                                                 \
   dequant_matmul_kernel<BITS, NXV, SF16><<<grid, 256, 0, st>>>(X, ldx, n, qw, words, scales, \
                                                          zeros, ng, g_idx, m, d, sgn, Y, ldy, \
-                                                         out_bf16, act)
+                                                         out_bf16, act, vec)
   if (nx == 1)
     GPTQ_DQ(1);
   else if (nx == 4)
