@@ -350,6 +350,333 @@ __global__ __launch_bounds__(256) void dequant_matmul_kernel(
   }
 }
 
+// ---------------------------------------------------------------------------
+// Many activation rows (n > 8): the same product on the matrix cores.
+//
+// A workgroup owns a tile of 128 activation rows x 128 weight rows; its four
+// waves hold 64 x 64 each as 4 x 4 fragments of v_mfma_f32_16x16x32_bf16.
+// The input dimension goes by in blocks of 64 columns (two 32-column steps),
+// the activations staged in LDS (double buffered, one barrier per block),
+// the codes loaded straight into registers a block ahead.
+//
+// Exactness: a weight is never rounded to bf16.  The B operand of a step is
+// an exact small number per code -- 8 + k / 2 for 2-, 3- and 4-bit codes
+// (the code in mantissa bits 3..6 under the exponent of 8), k itself for
+// 8-bit codes -- with k the unsigned code, or the signed code plus 2^(b-1).
+// Per group G the matrix cores form P = sum x B over the group's columns and
+// (one more product with B = 1) Xs = sum x; the group is folded into the
+// fp32 result when it ends:
+//   sum x Delta (c - z) = Delta (2 P - (16 + z) Xs)    (2-, 3-, 4-bit)
+//                       = Delta (P - z Xs)              (8-bit)
+// with z = 2^(b-1) for signed codes.  A step whose 32 columns share one group
+// (contiguous groups of a multiple of 32 columns, the whole-row grid) just
+// accumulates; a step that mixes groups (act-order with dynamic groups,
+// groups of 8) runs once per group present, its A operand masked to that
+// group's columns, and folds each at once.
+//
+// Within each 8-column run the activations are staged in the order the
+// code expansion produces pairs (4-bit: 0 2 4 6 1 3 5 7, 2-bit:
+// 0 4 1 5 2 6 3 7, 8-bit: natural); A and B agree on it, and the sum does
+// not depend on it.
+constexpr int kTm = 128;               // activation rows per workgroup
+constexpr int kTn = 128;               // weight rows per workgroup
+constexpr int kBk = 64;                // columns per LDS block
+constexpr int kAp = kBk + 8;           // padded LDS row (bf16)
+
+// Position, within an 8-column run, of the column whose activation sits at
+// staged slot e.
+template <int BITS>
+__device__ inline int run_col(int e) {
+  if (BITS == 8) return e;
+  if (BITS == 2) return (e >> 1) + 4 * (e & 1);
+  return 2 * (e & 3) + (e >> 2);      // 4-bit order, also used for 3-bit
+}
+
+// Reorders 8 bf16 activations (natural order in r) into the staged order.
+template <int BITS>
+__device__ inline uint4 stage_order(uint4 r) {
+  if (BITS == 8) return r;
+  if (BITS == 2)
+    return uint4{__builtin_amdgcn_perm(r.z, r.x, 0x05040100u),
+                 __builtin_amdgcn_perm(r.z, r.x, 0x07060302u),
+                 __builtin_amdgcn_perm(r.w, r.y, 0x05040100u),
+                 __builtin_amdgcn_perm(r.w, r.y, 0x07060302u)};
+  return uint4{__builtin_amdgcn_perm(r.y, r.x, 0x05040100u),
+               __builtin_amdgcn_perm(r.w, r.z, 0x05040100u),
+               __builtin_amdgcn_perm(r.y, r.x, 0x07060302u),
+               __builtin_amdgcn_perm(r.w, r.z, 0x07060302u)};
+}
+
+// Eight 4-bit codes (code i at bits 4i) as the bf16 pairs 8 + k/2 in the
+// staged order (0 2)(4 6)(1 3)(5 7).
+__device__ inline u32x4 expand4(uint32_t w) {
+  const uint32_t lo = (w << 3) & 0x78787878u, hi = (w >> 1) & 0x78787878u;
+  return u32x4{__builtin_amdgcn_perm(0x41414141u, lo, 0x04010400u),
+               __builtin_amdgcn_perm(0x41414141u, lo, 0x04030402u),
+               __builtin_amdgcn_perm(0x41414141u, hi, 0x04010400u),
+               __builtin_amdgcn_perm(0x41414141u, hi, 0x04030402u)};
+}
+
+// The B operand of one lane: the 8 codes of its run, already masked to
+// their bits (w0; w1 holds codes 4..7 for 8-bit), signed codes offset.
+template <int BITS>
+__device__ inline u32x4 expand_codes(uint32_t w0, uint32_t w1, int sgn) {
+  if (BITS == 4) return expand4(w0 ^ (sgn ? 0x88888888u : 0u));
+  if (BITS == 3) {
+    // spread the 3-bit fields to nibbles, then as 4-bit
+    uint32_t u = (w0 & 0xFFFu) | ((w0 & 0xFFF000u) << 4);
+    u = (u & 0x003F003Fu) | ((u & 0x0FC00FC0u) << 2);
+    u = (u & 0x07070707u) | ((u & 0x38383838u) << 1);
+    return expand4(u ^ (sgn ? 0x44444444u : 0u));
+  }
+  if (BITS == 2) {
+    const uint32_t v = w0 ^ (sgn ? 0xAAAAu : 0u);
+    return u32x4{__builtin_amdgcn_perm(0x41414141u, (v << 3) & 0x1818u, 0x04010400u),
+                 __builtin_amdgcn_perm(0x41414141u, (v << 1) & 0x1818u, 0x04010400u),
+                 __builtin_amdgcn_perm(0x41414141u, (v >> 1) & 0x1818u, 0x04010400u),
+                 __builtin_amdgcn_perm(0x41414141u, (v >> 3) & 0x1818u, 0x04010400u)};
+  }
+  // 8-bit: each code converted exactly to fp32, its upper half is the bf16
+  const uint32_t a = w0 ^ (sgn ? 0x80808080u : 0u), b = w1 ^ (sgn ? 0x80808080u : 0u);
+  const float f[8] = {float(a & 0xFFu), float((a >> 8) & 0xFFu), float((a >> 16) & 0xFFu),
+                      float(a >> 24), float(b & 0xFFu), float((b >> 8) & 0xFFu),
+                      float((b >> 16) & 0xFFu), float(b >> 24)};
+  u32x4 r;
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+    r[i] = __builtin_amdgcn_perm(__float_as_uint(f[2 * i + 1]), __float_as_uint(f[2 * i]),
+                                 0x07060302u);
+  return r;
+}
+
+// The code bits of 8-column run `ch` of a weight row (row pointer p,
+// `words` words), masked to the run: w0 (and w1 for 8-bit codes).  Runs past
+// the end read the last word (their activations are zero).
+template <int BITS>
+__device__ inline void load_run(const uint32_t* __restrict__ p, int64_t words, int64_t ch,
+                                uint32_t& w0, uint32_t& w1) {
+  if (BITS == 4) {
+    w0 = p[min<int64_t>(ch, words - 1)];
+    w1 = 0u;
+  } else if (BITS == 2) {
+    w0 = (p[min<int64_t>(ch >> 1, words - 1)] >> (16 * (ch & 1))) & 0xFFFFu;
+    w1 = 0u;
+  } else if (BITS == 8) {
+    w0 = p[min<int64_t>(2 * ch, words - 1)];
+    w1 = p[min<int64_t>(2 * ch + 1, words - 1)];
+  } else {
+    const int64_t bit = 24 * ch;
+    const int64_t i = min<int64_t>(bit >> 5, words - 1);
+    const uint32_t lo = p[i], hi = p[min<int64_t>(i + 1, words - 1)];
+    w0 = __builtin_amdgcn_alignbit(hi, lo, static_cast<uint32_t>(bit & 31)) & 0xFFFFFFu;
+    w1 = 0u;
+  }
+}
+
+// P += A B on v_mfma_f32_16x16x32_bf16 (the compiler's builtin, so that the
+// wait states between an MFMA and the instructions reading its result are
+// the compiler's to insert).
+__device__ inline void mfma_acc(f32x4& P, const u32x4& a, const u32x4& b) {
+  P = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a),
+                                              __builtin_bit_cast(bf16x8, b), P, 0, 0, 0);
+}
+
+template <int BITS, bool SF16>
+__global__ __launch_bounds__(256) void dequant_gemm_kernel(
+    const uint16_t* __restrict__ X, int64_t ldx, int64_t n,
+    const uint32_t* __restrict__ qw, int64_t words,
+    const void* __restrict__ scales, const uint8_t* __restrict__ zeros,
+    int64_t ng, const int32_t* __restrict__ g_idx, int64_t m, int64_t d,
+    int sgn, void* __restrict__ Y, int64_t ldy, int out_bf16, int act, int vec,
+    unsigned tiles_m, unsigned tiles) {
+  __shared__ __attribute__((aligned(16))) uint16_t as[2][kTm][kAp];
+  __shared__ int32_t gsh[2][kBk];
+  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+  const int q = lane >> 4, c16 = lane & 15;
+  // consecutive tiles share activation rows; spread them so that each
+  // XCD (blocks b, b + 8, ...) walks a contiguous range of tiles
+  unsigned tile = blockIdx.x;
+  const unsigned per = tiles / 8;
+  if (tile < 8 * per) tile = (tile % 8) * per + tile / 8;
+  const int64_t rb = int64_t(tile % tiles_m) * kTn;     // first weight row
+  const int64_t tb = int64_t(tile / tiles_m) * kTm;     // first activation row
+  const int wm = (wv & 1) * 64, wn = (wv >> 1) * 64;     // wave's offsets
+
+  // weight rows of the lane's B fragments (clamped; not stored past m)
+  const uint32_t* prow[4];
+  int64_t rowj[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    rowj[j] = min<int64_t>(rb + wn + 16 * j + c16, m - 1);
+    prow[j] = qw + rowj[j] * words;
+  }
+  constexpr bool kMagic = BITS != 8;
+  const float zsgn = static_cast<float>(1 << (BITS - 1));
+
+  f32x4 acc[4][4], P[4][4], Xs[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    Xs[i] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int j = 0; j < 4; ++j) acc[i][j] = P[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+  }
+  // the grid of the open group: 2 Delta (or Delta) and the zero term
+  float gs_s[4], gs_z[4];
+  int cur = -1;        // open group (uniform over the workgroup), -1: none
+
+  auto open_grid = [&](int G, float* s, float* z) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const float dl = load_scale<SF16>(scales, rowj[j] * ng + G);
+      const float zz = sgn ? zsgn : static_cast<float>(zeros[rowj[j] * ng + G]);
+      s[j] = kMagic ? 2.0f * dl : dl;
+      z[j] = kMagic ? 8.0f + 0.5f * zz : zz;
+    }
+  };
+  // fold the group's products into the result, and clear them
+  auto fold = [&](const float* s, const float* z) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+#pragma unroll
+        for (int v = 0; v < 4; ++v)
+          acc[i][j][v] = fmaf(s[j], fmaf(-z[j], Xs[i][v], P[i][j][v]), acc[i][j][v]);
+        P[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+      }
+      Xs[i] = f32x4{0.f, 0.f, 0.f, 0.f};
+    }
+  };
+
+  // ---- staging of one block's activations and group ids into registers
+  uint4 ax[4];
+  int32_t gx = 0;
+  auto fetch = [&](int64_t c0) {
+#pragma unroll
+    for (int h = 0; h < 4; ++h) {
+      const int u = tid + 256 * h;            // 8-column unit: row u / 8, run u % 8
+      const int64_t tok = tb + (u >> 3);
+      const int64_t cb = c0 + 8 * (u & 7);
+      uint4 v = uint4{0u, 0u, 0u, 0u};
+      if (tok < n) {
+        const uint16_t* src = X + tok * ldx + cb;
+        if ((vec & kVecX) && cb + 8 <= d) {
+          v = *reinterpret_cast<const uint4*>(src);
+        } else {
+          uint32_t e[8];
+#pragma unroll
+          for (int k = 0; k < 8; ++k) e[k] = cb + k < d ? src[k] : 0u;
+          v = uint4{e[0] | (e[1] << 16), e[2] | (e[3] << 16), e[4] | (e[5] << 16),
+                    e[6] | (e[7] << 16)};
+        }
+      }
+      ax[h] = stage_order<BITS>(v);
+    }
+    if (tid < kBk) gx = g_idx[min<int64_t>(c0 + tid, d - 1)];
+  };
+  auto store = [&](int buf) {
+#pragma unroll
+    for (int h = 0; h < 4; ++h) {
+      const int u = tid + 256 * h;
+      *reinterpret_cast<uint4*>(&as[buf][u >> 3][8 * (u & 7)]) = ax[h];
+    }
+    if (tid < kBk) gsh[buf][tid] = gx;
+  };
+  // codes of the lane's runs in both steps of a block
+  uint32_t cw[2][4][2];
+  auto fetch_codes = [&](int64_t c0) {
+#pragma unroll
+    for (int s = 0; s < 2; ++s)
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+        load_run<BITS>(prow[j], words, (c0 + 32 * s) / 8 + q, cw[s][j][0], cw[s][j][1]);
+  };
+
+  const int64_t nblk = (d + kBk - 1) / kBk;
+  fetch(0);
+  fetch_codes(0);
+  store(0);
+  __syncthreads();
+  const u32x4 ones = u32x4{0x3F803F80u, 0x3F803F80u, 0x3F803F80u, 0x3F803F80u};
+  for (int64_t blk = 0; blk < nblk; ++blk) {
+    const int buf = static_cast<int>(blk & 1);
+    const int64_t c0 = blk * kBk;
+    uint32_t cc[2][4][2];
+#pragma unroll
+    for (int s = 0; s < 2; ++s)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) { cc[s][j][0] = cw[s][j][0]; cc[s][j][1] = cw[s][j][1]; }
+    if (blk + 1 < nblk) {
+      fetch(c0 + kBk);
+      fetch_codes(c0 + kBk);
+    }
+    // a step past the end of the input runs on zero activations (its
+    // columns carry the last column's group id), so adds nothing
+#pragma unroll
+    for (int s = 0; s < 2; ++s) {
+      u32x4 B[4];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) B[j] = expand_codes<BITS>(cc[s][j][0], cc[s][j][1], sgn);
+      // the groups present among the step's 32 columns (lane l: column
+      // l % 32), one pass each, in the order of their first column; a pass
+      // masks the activations of the other groups' columns
+      const int gl = gsh[buf][32 * s + (lane & 31)];
+      int ge[8];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) ge[e] = gsh[buf][32 * s + 8 * q + run_col<BITS>(e)];
+      uint64_t left = 0xFFFFFFFFull;
+      do {
+        const int G = __shfl(gl, __builtin_ctzll(left));
+        const uint64_t in = __ballot(gl == G) & 0xFFFFFFFFull;
+        left &= ~in;
+        if (G != cur) {
+          if (cur >= 0) fold(gs_s, gs_z);
+          open_grid(G, gs_s, gs_z);
+          cur = G;
+        }
+        uint32_t mk[4] = {~0u, ~0u, ~0u, ~0u};
+        if (in != 0xFFFFFFFFull) {
+#pragma unroll
+          for (int p = 0; p < 4; ++p)
+            mk[p] = (ge[2 * p] == G ? 0x0000FFFFu : 0u) | (ge[2 * p + 1] == G ? 0xFFFF0000u : 0u);
+        }
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          u32x4 A = *reinterpret_cast<const u32x4*>(&as[buf][wm + 16 * i + c16][32 * s + 8 * q]);
+#pragma unroll
+          for (int p = 0; p < 4; ++p) A[p] &= mk[p];
+          mfma_acc(Xs[i], A, ones);
+#pragma unroll
+          for (int j = 0; j < 4; ++j) mfma_acc(P[i][j], A, B[j]);
+        }
+      } while (left);
+    }
+    if (blk + 1 < nblk) store(buf ^ 1);
+    __syncthreads();
+  }
+  if (cur >= 0) fold(gs_s, gs_z);
+
+  // ---- results: lane holds activation rows 4q + v of each 16-row fragment,
+  //      weight row c16 of each 16-column fragment
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int v = 0; v < 4; ++v) {
+      const int64_t tok = tb + wm + 16 * i + 4 * q + v;
+      if (tok >= n) continue;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int64_t r = rb + wn + 16 * j + c16;
+        if (r >= m) continue;
+        const int64_t e = tok * ldy + r;
+        if (out_bf16)
+          static_cast<uint16_t*>(Y)[e] = f32_to_bf16(activate(acc[i][j][v], act));
+        else
+          static_cast<float*>(Y)[e] = acc[i][j][v];
+      }
+    }
+}
+
 unsigned cdiv(int64_t a, int64_t b) { return static_cast<unsigned>((a + b - 1) / b); }
 
 template <int BITS, bool SF16>
@@ -358,11 +685,21 @@ gptq_status launch_bits(const uint16_t* X, int64_t ldx, int64_t n, const uint32_
                         int64_t ng, const int32_t* g_idx, int64_t m, int64_t d,
                         int sgn, void* Y, int64_t ldy, int out_bf16, int act,
                         hipStream_t st) {
+  const int vecx = (ldx % 8 == 0 && reinterpret_cast<uintptr_t>(X) % 16 == 0) ? kVecX : 0;
+  if (n > 8) {
+    const unsigned tiles_m = cdiv(m, kTn);
+    const unsigned tiles = tiles_m * cdiv(n, kTm);
+    dequant_gemm_kernel<BITS, SF16><<<tiles, 256, 0, st>>>(
+        X, ldx, n, qw, words, scales, zeros, ng, g_idx, m, d, sgn, Y, ldy, out_bf16, act, vecx,
+        tiles_m, tiles);
+    GPTQ_CHECK_LAUNCH();
+    return GPTQ_OK;
+  }
   const int nx = n <= 1 ? 1 : n <= 4 ? 4 : 8;
   const int64_t rows_wg = 4 * rows_per_wave(nx);
   const dim3 grid(cdiv(m, rows_wg), cdiv(n, nx));
   const int wbytes = BITS == 2 ? 8 : 16;       // wide code load of one segment
-  const int vec = ((ldx % 8 == 0 && reinterpret_cast<uintptr_t>(X) % 16 == 0) ? kVecX : 0) |
+  const int vec = vecx |
                   (reinterpret_cast<uintptr_t>(g_idx) % 16 == 0 ? kVecG : 0) |
                   ((words * 4 % wbytes == 0 && reinterpret_cast<uintptr_t>(qw) % wbytes == 0)
                        ? kVecW : 0);

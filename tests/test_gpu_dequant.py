@@ -74,7 +74,7 @@ LAYERS = [
 
 
 @pytest.mark.parametrize("case", LAYERS, ids=lambda c: "m{m}_d{d}_b{bits}_g{group_size}".format(**c))
-@pytest.mark.parametrize("n", [1, 3, 8, 21])
+@pytest.mark.parametrize("n", [1, 3, 8, 21, 130])
 def test_dequant_matmul_matches_oracle(dev, case, n):
     c = dict(case)
     m, d = c.pop("m"), c.pop("d")
@@ -100,7 +100,29 @@ def test_dequant_matmul_random_codes(dev, bits):
     scales = rng.uniform(0.001, 0.05, size=(m, ng)).astype(np.float32)
     zeros = rng.integers(0, 2 ** bits, size=(m, ng))
     g_idx = rng.integers(0, ng, size=d)
-    X = synth.lowrank_outlier_acts(d, 5, 53, f"dq/R/{bits}", "cpu")
+    for n in (5, 40):
+        X = synth.lowrank_outlier_acts(d, n, 53, f"dq/R/{bits}/{n}", "cpu")
+        _check(dev, X, packed, scales, zeros, g_idx, bits, g, False, m)
+        _check(dev, X, packed, scales, np.zeros_like(zeros), g_idx, bits, g, True, m)
+
+
+@pytest.mark.parametrize("bits", [2, 3, 4, 8])
+@pytest.mark.parametrize("g", [32, 96, 40, -1])
+def test_dequant_matmul_many_rows_contiguous_groups(dev, bits, g):
+    """Many activation rows (the matrix-core product): contiguous groups of
+    a multiple of 32 columns (every 32-column step inside one group), of 40
+    columns (steps straddling two groups), and the whole-row grid; two tiles
+    of activation rows and of weight rows, both ragged, d ragged against the
+    64-column blocks."""
+    rng = np.random.default_rng(100 + bits)
+    m, d, n = 260, 1000, 150
+    ng = -(-d // g) if g > 0 else 1
+    codes = rng.integers(0, 2 ** bits, size=(m, d))
+    packed = orc.pack_codes(codes, bits)
+    scales = rng.uniform(0.001, 0.05, size=(m, ng)).astype(np.float32)
+    zeros = rng.integers(0, 2 ** bits, size=(m, ng))
+    g_idx = np.arange(d) // g if g > 0 else np.zeros(d, dtype=np.int64)
+    X = synth.lowrank_outlier_acts(d, n, 55, f"dq/C/{bits}/{g}", "cpu")
     _check(dev, X, packed, scales, zeros, g_idx, bits, g, False, m)
     _check(dev, X, packed, scales, np.zeros_like(zeros), g_idx, bits, g, True, m)
 
@@ -116,7 +138,7 @@ def test_dequant_matmul_fp16_scales(dev, case):
     S = orc.hessian_sum(Xc.double().numpy())
     res = orc.gptq_layer(W.double().numpy(), S, 600, blocksize=128, **c)
     zeros = np.zeros_like(res.zeros) if res.signed else res.zeros
-    for n in (1, 8, 13):
+    for n in (1, 8, 13, 70):
         X = synth.lowrank_outlier_acts(d, n, 54, f"dq/H/{d}/{n}", "cpu")
         _check(dev, X, res.packed, res.scales, zeros, res.g_idx, c["bits"],
                c["group_size"], res.signed, m, f16=True)
