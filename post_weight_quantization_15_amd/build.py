@@ -27,8 +27,10 @@ HIPCC_FLAGS = [
 ]
 
 
-# Per-file additions (none at present).
-FILE_FLAGS: dict = {}
+# Per-file additions.  The matrix-core dequantizing product keeps its
+# partial products in ordinary VGPRs (the fold into the result reads them
+# every group; in the accumulation registers they would be copied out).
+FILE_FLAGS: dict = {"k_dequant.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1"]}
 
 
 def hipcc() -> str:

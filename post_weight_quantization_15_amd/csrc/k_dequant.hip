@@ -355,7 +355,7 @@ __global__ __launch_bounds__(256) void dequant_matmul_kernel(
 //
 // A workgroup owns a tile of 128 activation rows x 128 weight rows; its four
 // waves hold 64 x 64 each as 4 x 4 fragments of v_mfma_f32_16x16x32_bf16.
-// The input dimension goes by in blocks of 64 columns (two 32-column steps),
+// The input dimension goes by in blocks of 128 columns (four 32-column steps),
 // the activations staged in LDS (double buffered, one barrier per block),
 // the codes loaded straight into registers a block ahead.
 //
@@ -380,7 +380,7 @@ __global__ __launch_bounds__(256) void dequant_matmul_kernel(
 // not depend on it.
 constexpr int kTm = 128;               // activation rows per workgroup
 constexpr int kTn = 128;               // weight rows per workgroup
-constexpr int kBk = 64;                // columns per LDS block
+constexpr int kBk = 64;               // columns per LDS block
 constexpr int kAp = kBk + 8;           // padded LDS row (bf16)
 
 // Position, within an 8-column run, of the column whose activation sits at
@@ -489,8 +489,11 @@ __global__ __launch_bounds__(256) void dequant_gemm_kernel(
     int64_t ng, const int32_t* __restrict__ g_idx, int64_t m, int64_t d,
     int sgn, void* __restrict__ Y, int64_t ldy, int out_bf16, int act, int vec,
     unsigned tiles_m, unsigned tiles) {
+  constexpr int kSteps = kBk / 32;
+  constexpr int kUnits = kTm * kBk / 8 / 256;          // 8-column units per thread
   __shared__ __attribute__((aligned(16))) uint16_t as[2][kTm][kAp];
   __shared__ int32_t gsh[2][kBk];
+  __shared__ __attribute__((aligned(16))) int32_t desc[2][kSteps];
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
   const int q = lane >> 4, c16 = lane & 15;
   // consecutive tiles share activation rows; spread them so that each
@@ -503,13 +506,9 @@ __global__ __launch_bounds__(256) void dequant_gemm_kernel(
   const int wm = (wv & 1) * 64, wn = (wv >> 1) * 64;     // wave's offsets
 
   // weight rows of the lane's B fragments (clamped; not stored past m)
-  const uint32_t* prow[4];
   int64_t rowj[4];
 #pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    rowj[j] = min<int64_t>(rb + wn + 16 * j + c16, m - 1);
-    prow[j] = qw + rowj[j] * words;
-  }
+  for (int j = 0; j < 4; ++j) rowj[j] = min<int64_t>(rb + wn + 16 * j + c16, m - 1);
   constexpr bool kMagic = BITS != 8;
   const float zsgn = static_cast<float>(1 << (BITS - 1));
 
@@ -549,16 +548,22 @@ __global__ __launch_bounds__(256) void dequant_gemm_kernel(
   };
 
   // ---- staging of one block's activations and group ids into registers
-  uint4 ax[4];
+  uint4 ax[kUnits];
   int32_t gx = 0;
+  // a block whose activation rows all exist, 16-byte aligned and inside
+  // the input, stages with unconditional wide loads
+  const bool full_rows = (vec & kVecX) && tb + kTm <= n;
   auto fetch = [&](int64_t c0) {
+    const bool wide = full_rows && c0 + kBk <= d;
 #pragma unroll
-    for (int h = 0; h < 4; ++h) {
-      const int u = tid + 256 * h;            // 8-column unit: row u / 8, run u % 8
-      const int64_t tok = tb + (u >> 3);
-      const int64_t cb = c0 + 8 * (u & 7);
+    for (int h = 0; h < kUnits; ++h) {
+      const int u = tid + 256 * h;   // 8-column unit: row u / (kBk/8), run u % (kBk/8)
+      const int64_t tok = tb + u / (kBk / 8);
+      const int64_t cb = c0 + 8 * (u % (kBk / 8));
       uint4 v = uint4{0u, 0u, 0u, 0u};
-      if (tok < n) {
+      if (wide) {
+        v = *reinterpret_cast<const uint4*>(X + tok * ldx + cb);
+      } else if (tok < n) {
         const uint16_t* src = X + tok * ldx + cb;
         if ((vec & kVecX) && cb + 8 <= d) {
           v = *reinterpret_cast<const uint4*>(src);
@@ -574,22 +579,38 @@ __global__ __launch_bounds__(256) void dequant_gemm_kernel(
     }
     if (tid < kBk) gx = g_idx[min<int64_t>(c0 + tid, d - 1)];
   };
+  // LDS writes of the staged block; the waves holding group ids also write
+  // one descriptor per 32-column step: its group when all its columns share
+  // one, else -1
   auto store = [&](int buf) {
 #pragma unroll
-    for (int h = 0; h < 4; ++h) {
+    for (int h = 0; h < kUnits; ++h) {
       const int u = tid + 256 * h;
-      *reinterpret_cast<uint4*>(&as[buf][u >> 3][8 * (u & 7)]) = ax[h];
+      *reinterpret_cast<uint4*>(&as[buf][u / (kBk / 8)][8 * (u % (kBk / 8))]) = ax[h];
     }
-    if (tid < kBk) gsh[buf][tid] = gx;
+    if (tid < kBk) {
+      gsh[buf][tid] = gx;
+      const int half = lane & 32;
+      const int G0 = __shfl(gx, half);
+      const uint64_t same = __ballot(gx == G0);
+      if ((lane & 31) == 0)
+        desc[buf][tid >> 5] = ((same >> half) & 0xFFFFFFFFull) == 0xFFFFFFFFull ? G0 : -1;
+    }
   };
-  // codes of the lane's runs in both steps of a block
-  uint32_t cw[2][4][2];
+  // codes of the lane's runs in the steps of a block
+  uint32_t cw[kSteps][4][2];
   auto fetch_codes = [&](int64_t c0) {
 #pragma unroll
-    for (int s = 0; s < 2; ++s)
+    for (int s = 0; s < kSteps; ++s)
 #pragma unroll
       for (int j = 0; j < 4; ++j)
-        load_run<BITS>(prow[j], words, (c0 + 32 * s) / 8 + q, cw[s][j][0], cw[s][j][1]);
+        load_run<BITS>(qw + rowj[j] * words, words, (c0 + 32 * s) / 8 + q, cw[s][j][0],
+                       cw[s][j][1]);
+  };
+  auto read_a = [&](int buf, int s, u32x4* A) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      A[i] = *reinterpret_cast<const u32x4*>(&as[buf][wm + 16 * i + c16][32 * s + 8 * q]);
   };
 
   const int64_t nblk = (d + kBk - 1) / kBk;
@@ -601,33 +622,42 @@ __global__ __launch_bounds__(256) void dequant_gemm_kernel(
   for (int64_t blk = 0; blk < nblk; ++blk) {
     const int buf = static_cast<int>(blk & 1);
     const int64_t c0 = blk * kBk;
-    uint32_t cc[2][4][2];
+    int dsc[kSteps];
 #pragma unroll
-    for (int s = 0; s < 2; ++s)
+    for (int s = 0; s < kSteps; ++s) dsc[s] = __builtin_amdgcn_readfirstlane(desc[buf][s]);
+    u32x4 An[4];
+    read_a(buf, 0, An);
+    uint32_t cc[kSteps][4][2];
+#pragma unroll
+    for (int s = 0; s < kSteps; ++s)
 #pragma unroll
       for (int j = 0; j < 4; ++j) { cc[s][j][0] = cw[s][j][0]; cc[s][j][1] = cw[s][j][1]; }
     if (blk + 1 < nblk) {
       fetch(c0 + kBk);
       fetch_codes(c0 + kBk);
     }
-    // a step past the end of the input runs on zero activations (its
-    // columns carry the last column's group id), so adds nothing
 #pragma unroll
-    for (int s = 0; s < 2; ++s) {
+    for (int s = 0; s < kSteps; ++s) {
+      if (c0 + 32 * s >= d) break;       // steps past the end of the input
+      u32x4 A[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) A[i] = An[i];
+      if (s + 1 < kSteps) read_a(buf, s + 1, An);    // next step's fragments
       u32x4 B[4];
 #pragma unroll
       for (int j = 0; j < 4; ++j) B[j] = expand_codes<BITS>(cc[s][j][0], cc[s][j][1], sgn);
-      // the groups present among the step's 32 columns (lane l: column
-      // l % 32), one pass each, in the order of their first column; a pass
-      // masks the activations of the other groups' columns
-      const int gl = gsh[buf][32 * s + (lane & 31)];
-      int ge[8];
-#pragma unroll
-      for (int e = 0; e < 8; ++e) ge[e] = gsh[buf][32 * s + 8 * q + run_col<BITS>(e)];
+      // the groups present among the step's 32 columns, one pass each in
+      // the order of their first column (one pass when the descriptor names
+      // the step's single group); a pass masks the activations of the other
+      // groups' columns (lane l of the group-id read: column l % 32)
+      const int Gs = dsc[s];
+      int gl = Gs;
+      if (Gs < 0) gl = gsh[buf][32 * s + (lane & 31)];
       uint64_t left = 0xFFFFFFFFull;
       do {
-        const int G = __shfl(gl, __builtin_ctzll(left));
-        const uint64_t in = __ballot(gl == G) & 0xFFFFFFFFull;
+        const int G = Gs >= 0 ? Gs
+                              : __builtin_amdgcn_readfirstlane(__shfl(gl, __builtin_ctzll(left)));
+        const uint64_t in = Gs >= 0 ? 0xFFFFFFFFull : (__ballot(gl == G) & 0xFFFFFFFFull);
         left &= ~in;
         if (G != cur) {
           if (cur >= 0) fold(gs_s, gs_z);
@@ -637,17 +667,20 @@ __global__ __launch_bounds__(256) void dequant_gemm_kernel(
         uint32_t mk[4] = {~0u, ~0u, ~0u, ~0u};
         if (in != 0xFFFFFFFFull) {
 #pragma unroll
-          for (int p = 0; p < 4; ++p)
-            mk[p] = (ge[2 * p] == G ? 0x0000FFFFu : 0u) | (ge[2 * p + 1] == G ? 0xFFFF0000u : 0u);
+          for (int p = 0; p < 4; ++p) {
+            const int e0 = 32 * s + 8 * q + run_col<BITS>(2 * p);
+            const int e1 = 32 * s + 8 * q + run_col<BITS>(2 * p + 1);
+            mk[p] = (gsh[buf][e0] == G ? 0x0000FFFFu : 0u) | (gsh[buf][e1] == G ? 0xFFFF0000u : 0u);
+          }
         }
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-          u32x4 A = *reinterpret_cast<const u32x4*>(&as[buf][wm + 16 * i + c16][32 * s + 8 * q]);
+          u32x4 Am = A[i];
 #pragma unroll
-          for (int p = 0; p < 4; ++p) A[p] &= mk[p];
-          mfma_acc(Xs[i], A, ones);
+          for (int p = 0; p < 4; ++p) Am[p] &= mk[p];
+          mfma_acc(Xs[i], Am, ones);
 #pragma unroll
-          for (int j = 0; j < 4; ++j) mfma_acc(P[i][j], A, B[j]);
+          for (int j = 0; j < 4; ++j) mfma_acc(P[i][j], Am, B[j]);
         }
       } while (left);
     }
