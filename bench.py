@@ -302,6 +302,29 @@ def next_rows(gq, torch, synth, dev):
     out["dequant_matmul"] = {"shape": f"{m}x{d} g{g}, bf16 activations, fp32 out",
                              "bound": "hbm", "peak_GB/s": PEAK_HBM_GBS, "runs": dq}
     torch.cuda.empty_cache()
+    # ---- the same product at many activation rows (matrix cores): the
+    # layer-by-layer driver's propagation shape, 65536 tokens x 4096 x 4096
+    n, m, d = 65536, 4096, 4096
+    X = torch.randn(n, d, device=dev, generator=gen).to(torch.bfloat16)
+    Y = torch.empty(n, m, device=dev)
+    gm = []
+    for bits, g in ((4, 128), (4, -1), (2, 128), (8, 128)):
+        ng = 1 if g == -1 else d // g
+        qw = torch.randint(-2 ** 31, 2 ** 31 - 1, (m, d * bits // 32), dtype=torch.int32,
+                           device=dev, generator=gen)
+        sc = torch.rand(m, ng, device=dev, generator=gen) * 0.01 + 0.001
+        zp = torch.randint(0, 2 ** bits, (m, ng), dtype=torch.uint8, device=dev, generator=gen)
+        gi = (torch.zeros(d, device=dev) if g == -1 else
+              torch.arange(d, device=dev) // g).to(torch.int32)
+        ms = _event_ms(torch, lambda: gq.gptq_dequant_matmul(X, qw, sc, zp, gi, bits, g, Y=Y), 3)
+        tf = 2.0 * n * m * d / (ms * 1e-3) / 1e12
+        gm.append({"bits": bits, "group_size": g, "ms": round(ms, 3), "TFLOP/s": round(tf, 1),
+                   "frac_bf16": round(tf / PEAK_BF16_TFLOPS, 4)})
+        del qw, sc, zp, gi
+    out["dequant_gemm"] = {"shape": f"{n} tokens x {m}x{d}, bf16 activations, fp32 out",
+                           "bound": "mfma", "peak_TFLOP/s": PEAK_BF16_TFLOPS, "runs": gm}
+    del X, Y
+    torch.cuda.empty_cache()
     # ---- quantizer variants on the attention-projection layer (S given)
     L = synth.attn_proj_layer(dev)
     W, X = L["W"], L["X"]

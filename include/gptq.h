@@ -231,7 +231,8 @@ gptq_status gptq_quantize_layer(const void* W, gptq_dtype w_dtype, int64_t m,
  *   (signed_codes = 1: code sign-extended from `bits` bits, zeros ignored).
  *
  * X: bf16 activations [n, d] token-major, row stride ldx >= d (GPTQ_BF16
- *    only); 0 <= n <= 524280 (tiles of up to 8 rows share one weight pass).
+ *    only); 0 <= n <= 524280.  Up to 8 rows: one weight pass on the vector
+ *    units; more: bf16 matrix cores on tiles of 128 rows.
  * qweight, scales, zeros, g_idx: as gptq_quantize_layer writes them
  *    (qweight [m, ceil(d*bits/32)] uint32, scales / zeros uint8 [m, n_g]
  *    with n_g from group_size, g_idx int32 [d], values < n_g).
@@ -239,7 +240,10 @@ gptq_status gptq_quantize_layer(const void* W, gptq_dtype w_dtype, int64_t m,
  *    16-bit storage of the steps: fp16 scales [m, n_g], e.g. the fp32 ones
  *    rounded to nearest; each is widened exactly to fp32 in the kernel).
  * Y: fp32 [n, m], row stride ldy >= m; fully overwritten.
- * Sums in fp32 (each group's grid factored out of its 8-column runs).
+ * Sums in fp32, every product of an activation and a code exact: each
+ * group's grid is factored out of the group's sums (Delta (sum x c - z sum x)),
+ * the codes entering the products as exact small numbers, never as rounded
+ * weights.
  * Errors: INVALID_ARG (bad sizes, dtype, scale_dtype, bits, group_size,
  *         NULL pointers when n > 0); HIP.  Allocates nothing; no workspace.
  * ------------------------------------------------------------------------- */

@@ -7,11 +7,14 @@ dynamic groups with act-order, static groups, whole-row grids, signed
 symmetric codes) and from seeded random codes; activations are bf16; the
 steps fp32, or fp16 (the compact storage).
 
-Tolerance from the arithmetic: the kernel forms, per 8-column run sharing
-one grid, Delta (sum x c - z sum x), and adds the runs in an fp32 running
-sum; every term it rounds is bounded by |x_c| Delta (|c| + |z|), so with at
-most d + 16 roundings on the way |dY| <= (d + 16) 2^-24 sum_c |x_c|
-Delta_{r,g(c)} (|c_rc| + |z_{r,g(c)}|), entrywise (signed codes: z = 0).
+Tolerance from the arithmetic: both kernels (up to 8 activation rows on the
+vector units, more on the matrix cores) form, per run of columns sharing one
+grid (8-column runs; a group's 32-column steps), Delta (sum x c - z sum x)
+with exact products, and add the runs in an fp32 running sum; every term
+rounded is bounded by |x_c| Delta (|c| + |z|) (up to the small constant
+offset of the codes' exact encoding), so with at most d + 16 roundings on
+the way |dY| <= (d + 16) 2^-24 sum_c |x_c| Delta_{r,g(c)} (|c_rc| +
+|z_{r,g(c)}|), entrywise (signed codes: z = 0).
 """
 
 import numpy as np
