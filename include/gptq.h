@@ -231,8 +231,8 @@ gptq_status gptq_quantize_layer(const void* W, gptq_dtype w_dtype, int64_t m,
  *   (signed_codes = 1: code sign-extended from `bits` bits, zeros ignored).
  *
  * X: bf16 activations [n, d] token-major, row stride ldx >= d (GPTQ_BF16
- *    only); 0 <= n <= 524280.  Up to 8 rows: one weight pass on the vector
- *    units; more: bf16 matrix cores on tiles of 128 rows.
+ *    only); 0 <= n <= 524280.  Up to 16 rows: the vector units, one weight
+ *    pass per 8 rows; more: bf16 matrix cores on tiles of 128 rows.
  * qweight, scales, zeros, g_idx: as gptq_quantize_layer writes them
  *    (qweight [m, ceil(d*bits/32)] uint32, scales / zeros uint8 [m, n_g]
  *    with n_g from group_size, g_idx int32 [d], values < n_g).

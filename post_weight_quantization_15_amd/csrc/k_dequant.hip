@@ -351,7 +351,9 @@ __global__ __launch_bounds__(256) void dequant_matmul_kernel(
 }
 
 // ---------------------------------------------------------------------------
-// Many activation rows (n > 8): the same product on the matrix cores.
+// Many activation rows (n > 16; up to 16 the vector kernel's passes of 8 rows
+// take less time than a mostly empty 128-row tile): the same product on the
+// matrix cores.
 //
 // A workgroup owns a tile of 128 activation rows x 128 weight rows; its four
 // waves hold 64 x 64 each as 4 x 4 fragments of v_mfma_f32_16x16x32_bf16.
@@ -719,7 +721,7 @@ gptq_status launch_bits(const uint16_t* X, int64_t ldx, int64_t n, const uint32_
                         int sgn, void* Y, int64_t ldy, int out_bf16, int act,
                         hipStream_t st) {
   const int vecx = (ldx % 8 == 0 && reinterpret_cast<uintptr_t>(X) % 16 == 0) ? kVecX : 0;
-  if (n > 8) {
+  if (n > 16) {
     const unsigned tiles_m = cdiv(m, kTn);
     const unsigned tiles = tiles_m * cdiv(n, kTm);
     dequant_gemm_kernel<BITS, SF16><<<tiles, 256, 0, st>>>(

@@ -7,7 +7,7 @@ dynamic groups with act-order, static groups, whole-row grids, signed
 symmetric codes) and from seeded random codes; activations are bf16; the
 steps fp32, or fp16 (the compact storage).
 
-Tolerance from the arithmetic: both kernels (up to 8 activation rows on the
+Tolerance from the arithmetic: both kernels (up to 16 activation rows on the
 vector units, more on the matrix cores) form, per run of columns sharing one
 grid (8-column runs; a group's 32-column steps), Delta (sum x c - z sum x)
 with exact products, and add the runs in an fp32 running sum; every term
