@@ -40,6 +40,7 @@ import numpy as np
 import pytest
 import torch
 
+import conftest
 import oracle as orc
 import post_weight_quantization_15_amd as gq
 import synth
@@ -56,9 +57,9 @@ ALL_ROWS = os.environ.get("GPTQ_FULLSIZE_ALL_ROWS", "") == "1"
 
 
 def say(msg):
-    """Progress line on the process's own stderr (left alone by pytest's
-    output capture), so that a long comparison is seen to progress."""
-    print(msg, file=sys.__stderr__, flush=True)
+    """Progress line on stderr past pytest's output capture, so that a long
+    comparison is seen to progress."""
+    conftest.progress(msg)
 
 
 def row_sample(m, nrows, seed):
