@@ -220,67 +220,77 @@ __global__ __launch_bounds__(256) void dequant_matmul_kernel(
 #pragma unroll
           for (int k = 0; k < NX; ++k) {
             float t = 0.0f;
+            if (BITS == 4 || BITS == 2) {
+              // the activation pairs against bf16 ones (0x3F80 = 1.0)
 #pragma unroll
-            for (int i = 0; i < 8; ++i) t += xv[k][i];
+              for (int i = 0; i < 4; ++i) t = dot2_bf16(xp[k][i], 0x3F803F80u, t);
+            } else {
+#pragma unroll
+              for (int i = 0; i < 8; ++i) t += xv[k][i];
+            }
             xsum[k] = t;
           }
           if (G != Gp) {
 #pragma unroll
             for (int r = 0; r < kRowsPerWave; ++r) {
               sc[r] = load_scale<SF16>(scales, rows[r] * ng + G);
-              zc[r] = static_cast<float>(zeros[rows[r] * ng + G]);
+              // 4- and 2-bit: the zero term 16 + z of the expansion below
+              // (signed codes: z = 8 or 2); other widths: z itself
+              const float z = static_cast<float>(zeros[rows[r] * ng + G]);
+              zc[r] = BITS == 4 ? 16.0f + (sgn ? 8.0f : z)
+                    : BITS == 2 ? 16.0f + (sgn ? 2.0f : z) : z;
             }
             Gp = G;
           }
           if (BITS == 4) {
             // the sub-block's 8 codes are word sb of the segment; each code
-            // k becomes the bf16 value 8 + k / 2 (exponent of 8, k in
+            // k becomes the bf16 value 16 + k (exponent of 16: 0x4180, k in
             // mantissa bits 3..6), two per register, and meets the matching
             // activation pair in one fp32-accumulating dot product:
-            // t = sum x (8 + k / 2), so sum x (k - z) = 2 t - (16 + z) sum x.
+            // t = sum x (16 + k), so sum x (k - z) = t - (16 + z) sum x.
             // Signed codes: k = c ^ 8 = c_s + 8, i.e. the same with z = 8.
 #pragma unroll
             for (int r = 0; r < kRowsPerWave; ++r) {
               const uint32_t wr = w[r][sb % BITS] ^ (sgn ? 0x88888888u : 0u);
-              const uint32_t lo = (wr << 3) & 0x78787878u;   // codes 0, 2, 4, 6
-              const uint32_t hi = (wr >> 1) & 0x78787878u;   // codes 1, 3, 5, 7
+              const uint32_t lo = ((wr << 3) & 0x78787878u) | 0x80808080u;   // codes 0, 2, 4, 6
+              const uint32_t hi = ((wr >> 1) & 0x78787878u) | 0x80808080u;   // codes 1, 3, 5, 7
               const uint32_t p02 = __builtin_amdgcn_perm(0x41414141u, lo, 0x04010400u);
               const uint32_t p46 = __builtin_amdgcn_perm(0x41414141u, lo, 0x04030402u);
               const uint32_t p13 = __builtin_amdgcn_perm(0x41414141u, hi, 0x04010400u);
               const uint32_t p57 = __builtin_amdgcn_perm(0x41414141u, hi, 0x04030402u);
-              const float zo = 16.0f + (sgn ? 8.0f : zc[r]);
 #pragma unroll
               for (int k = 0; k < NX; ++k) {
                 float t = dot2_bf16(p02, xp[k][0], 0.0f);
                 t = dot2_bf16(p46, xp[k][1], t);
                 t = dot2_bf16(p13, xp[k][2], t);
                 t = dot2_bf16(p57, xp[k][3], t);
-                acc[r][k] = fmaf(sc[r], fmaf(-zo, xsum[k], 2.0f * t), acc[r][k]);
+                acc[r][k] = fmaf(sc[r], fmaf(-zc[r], xsum[k], t), acc[r][k]);
               }
             }
           } else if (BITS == 2) {
             // the sub-block's 8 codes are half sb % 2 of word sb / 2; code j
-            // (bits 2j) goes to mantissa bits 3..4 of a bf16 8 + k / 2 as
+            // (bits 2j) goes to mantissa bits 3..4 of a bf16 16 + k as
             // above, pairs (c0, c4), (c1, c5), (c2, c6), (c3, c7).  Signed
             // codes: k = c ^ 2 = c_s + 2.
 #pragma unroll
             for (int r = 0; r < kRowsPerWave; ++r) {
               const uint32_t v = ((w[r][(sb / 2) % BITS] >> (16 * (sb % 2))) & 0xFFFFu) ^
                                  (sgn ? 0xAAAAu : 0u);
-              const uint32_t t04 = (v << 3) & 0x1818u, t15 = (v << 1) & 0x1818u;
-              const uint32_t t26 = (v >> 1) & 0x1818u, t37 = (v >> 3) & 0x1818u;
+              const uint32_t t04 = ((v << 3) & 0x1818u) | 0x8080u;
+              const uint32_t t15 = ((v << 1) & 0x1818u) | 0x8080u;
+              const uint32_t t26 = ((v >> 1) & 0x1818u) | 0x8080u;
+              const uint32_t t37 = ((v >> 3) & 0x1818u) | 0x8080u;
               const uint32_t p04 = __builtin_amdgcn_perm(0x41414141u, t04, 0x04010400u);
               const uint32_t p15 = __builtin_amdgcn_perm(0x41414141u, t15, 0x04010400u);
               const uint32_t p26 = __builtin_amdgcn_perm(0x41414141u, t26, 0x04010400u);
               const uint32_t p37 = __builtin_amdgcn_perm(0x41414141u, t37, 0x04010400u);
-              const float zo = 16.0f + (sgn ? 2.0f : zc[r]);
 #pragma unroll
               for (int k = 0; k < NX; ++k) {
                 float t = dot2_bf16(p04, xp[k][0], 0.0f);
                 t = dot2_bf16(p15, xp[k][1], t);
                 t = dot2_bf16(p26, xp[k][2], t);
                 t = dot2_bf16(p37, xp[k][3], t);
-                acc[r][k] = fmaf(sc[r], fmaf(-zo, xsum[k], 2.0f * t), acc[r][k]);
+                acc[r][k] = fmaf(sc[r], fmaf(-zc[r], xsum[k], t), acc[r][k]);
               }
             }
           } else {
