@@ -362,91 +362,79 @@ __global__ __launch_bounds__(256) void dequant_matmul_kernel(
 
 // ---------------------------------------------------------------------------
 // Many activation rows (n > 16; up to 16 the vector kernel's passes of 8 rows
-// take less time than a mostly empty 128-row tile): the same product on the
-// matrix cores.
+// take less time than a mostly empty tile): the same product on the matrix
+// cores.
 //
-// A workgroup owns a tile of 128 activation rows x 128 weight rows; its four
-// waves hold 64 x 64 each as 4 x 4 fragments of v_mfma_f32_16x16x32_bf16.
-// The input dimension goes by in blocks of 128 columns (four 32-column steps),
-// the activations staged in LDS (double buffered, one barrier per block),
-// the codes loaded straight into registers a block ahead.
+// A workgroup of eight waves (two per SIMD, so that one wave's waits and
+// VALU work overlap the other's MFMAs) owns a tile of 256 activation rows x
+// 128 weight rows; wave w holds activation rows 64 (w % 4) .. + 63 and weight
+// rows 64 (w / 4) .. + 63 as 4 x 4 fragments of v_mfma_f32_16x16x32_bf16.
+// The input dimension goes by in blocks of 64 columns (two 32-column steps),
+// double buffered in LDS with one barrier per block:
+//  * activations: global_load_lds_dwordx4 straight into LDS (no registers),
+//    a block ahead; blocks at the edges of the input (rows past n, columns
+//    past d, unaligned rows) go through registers, zero-filled;
+//  * codes: loaded into registers a block ahead, expanded by the whole
+//    workgroup into bf16 B operands in LDS (each code once per workgroup).
+// Both are stored as 16-byte units (8 columns) of a row, unit c of row r at
+// c ^ ((r / 2) % 8): the MFMA fragment reads (16 consecutive rows, one unit
+// each) then touch all 16 bank groups once, and each 8-row direct load
+// still fills every row with its 8 units (128 contiguous bytes).
 //
-// Exactness: a weight is never rounded to bf16.  The B operand of a step is
-// an exact small number per code -- 8 + k / 2 for 2-, 3- and 4-bit codes
-// (the code in mantissa bits 3..6 under the exponent of 8), k itself for
-// 8-bit codes -- with k the unsigned code, or the signed code plus 2^(b-1).
-// Per group G the matrix cores form P = sum x B over the group's columns and
-// (one more product with B = 1) Xs = sum x; the group is folded into the
-// fp32 result when it ends:
-//   sum x Delta (c - z) = Delta (2 P - (16 + z) Xs)    (2-, 3-, 4-bit)
-//                       = Delta (P - z Xs)              (8-bit)
+// Exactness: a weight is never rounded to bf16.  B holds an exact small
+// number per code -- 16 + k for 2-, 3- and 4-bit codes (the code in mantissa
+// bits 3..6 under the exponent of 16), k itself for 8-bit codes -- with k the
+// unsigned code, or the signed code plus 2^(b-1).  Per group G the matrix
+// cores form P = sum x B over the group's columns and (one more product with
+// B = 1) Xs = sum x; the group is folded into the fp32 result when it ends:
+//   sum x Delta (c - z) = Delta (P - (16 + z) Xs)    (2-, 3-, 4-bit)
+//                       = Delta (P - z Xs)            (8-bit)
 // with z = 2^(b-1) for signed codes.  A step whose 32 columns share one group
 // (contiguous groups of a multiple of 32 columns, the whole-row grid) just
 // accumulates; a step that mixes groups (act-order with dynamic groups,
 // groups of 8) runs once per group present, its A operand masked to that
 // group's columns, and folds each at once.
-//
-// Within each 8-column run the activations are staged in the order the
-// code expansion produces pairs (4-bit: 0 2 4 6 1 3 5 7, 2-bit:
-// 0 4 1 5 2 6 3 7, 8-bit: natural); A and B agree on it, and the sum does
-// not depend on it.
-constexpr int kTm = 128;               // activation rows per workgroup
+constexpr int kTm = 256;               // activation rows per workgroup
 constexpr int kTn = 128;               // weight rows per workgroup
-constexpr int kBk = 64;               // columns per LDS block
-constexpr int kAp = kBk + 8;           // padded LDS row (bf16)
+constexpr int kBk = 64;                // columns per LDS block
+constexpr int kGemmThreads = 512;      // eight waves
+constexpr int kUnitsA = kTm * kBk / 8; // 16-byte units of a block's activations
+constexpr int kUnitsB = kTn * kBk / 8; // and of its expanded codes
 
-// Position, within an 8-column run, of the column whose activation sits at
-// staged slot e.
-template <int BITS>
-__device__ inline int run_col(int e) {
-  if (BITS == 8) return e;
-  if (BITS == 2) return (e >> 1) + 4 * (e & 1);
-  return 2 * (e & 3) + (e >> 2);      // 4-bit order, also used for 3-bit
+// LDS byte offset of unit c (8 columns) of row r of a block.
+__device__ inline uint32_t unit_off(int r, int c) {
+  return static_cast<uint32_t>((r * (kBk / 8) + (c ^ ((r >> 1) & 7))) * 16);
 }
 
-// Reorders 8 bf16 activations (natural order in r) into the staged order.
-template <int BITS>
-__device__ inline uint4 stage_order(uint4 r) {
-  if (BITS == 8) return r;
-  if (BITS == 2)
-    return uint4{__builtin_amdgcn_perm(r.z, r.x, 0x05040100u),
-                 __builtin_amdgcn_perm(r.z, r.x, 0x07060302u),
-                 __builtin_amdgcn_perm(r.w, r.y, 0x05040100u),
-                 __builtin_amdgcn_perm(r.w, r.y, 0x07060302u)};
-  return uint4{__builtin_amdgcn_perm(r.y, r.x, 0x05040100u),
-               __builtin_amdgcn_perm(r.w, r.z, 0x05040100u),
-               __builtin_amdgcn_perm(r.y, r.x, 0x07060302u),
-               __builtin_amdgcn_perm(r.w, r.z, 0x07060302u)};
+// Eight codes in nibbles (code i at bits 4i) as four bf16 pairs 16 + k in
+// natural order (codes 2p, 2p + 1 in pair p).
+__device__ inline u32x4 expand_nibbles(uint32_t w) {
+  const uint32_t lo = ((w << 3) & 0x78787878u) | 0x80808080u;   // codes 0, 2, 4, 6
+  const uint32_t hi = ((w >> 1) & 0x78787878u) | 0x80808080u;   // codes 1, 3, 5, 7
+  return u32x4{__builtin_amdgcn_perm(hi, lo, 0x0C040C00u) | 0x41004100u,
+               __builtin_amdgcn_perm(hi, lo, 0x0C050C01u) | 0x41004100u,
+               __builtin_amdgcn_perm(hi, lo, 0x0C060C02u) | 0x41004100u,
+               __builtin_amdgcn_perm(hi, lo, 0x0C070C03u) | 0x41004100u};
 }
 
-// Eight 4-bit codes (code i at bits 4i) as the bf16 pairs 8 + k/2 in the
-// staged order (0 2)(4 6)(1 3)(5 7).
-__device__ inline u32x4 expand4(uint32_t w) {
-  const uint32_t lo = (w << 3) & 0x78787878u, hi = (w >> 1) & 0x78787878u;
-  return u32x4{__builtin_amdgcn_perm(0x41414141u, lo, 0x04010400u),
-               __builtin_amdgcn_perm(0x41414141u, lo, 0x04030402u),
-               __builtin_amdgcn_perm(0x41414141u, hi, 0x04010400u),
-               __builtin_amdgcn_perm(0x41414141u, hi, 0x04030402u)};
-}
-
-// The B operand of one lane: the 8 codes of its run, already masked to
-// their bits (w0; w1 holds codes 4..7 for 8-bit), signed codes offset.
+// The B operand of one 8-column run: its codes (w0; w1 holds codes 4..7 of
+// 8-bit codes) as exact bf16 numbers, natural order.
 template <int BITS>
-__device__ inline u32x4 expand_codes(uint32_t w0, uint32_t w1, int sgn) {
-  if (BITS == 4) return expand4(w0 ^ (sgn ? 0x88888888u : 0u));
+__device__ inline u32x4 expand_run(uint32_t w0, uint32_t w1, int sgn) {
+  if (BITS == 4) return expand_nibbles(w0 ^ (sgn ? 0x88888888u : 0u));
   if (BITS == 3) {
-    // spread the 3-bit fields to nibbles, then as 4-bit
+    // spread the 3-bit fields to nibbles
     uint32_t u = (w0 & 0xFFFu) | ((w0 & 0xFFF000u) << 4);
     u = (u & 0x003F003Fu) | ((u & 0x0FC00FC0u) << 2);
     u = (u & 0x07070707u) | ((u & 0x38383838u) << 1);
-    return expand4(u ^ (sgn ? 0x44444444u : 0u));
+    return expand_nibbles(u ^ (sgn ? 0x44444444u : 0u));
   }
   if (BITS == 2) {
-    const uint32_t v = w0 ^ (sgn ? 0xAAAAu : 0u);
-    return u32x4{__builtin_amdgcn_perm(0x41414141u, (v << 3) & 0x1818u, 0x04010400u),
-                 __builtin_amdgcn_perm(0x41414141u, (v << 1) & 0x1818u, 0x04010400u),
-                 __builtin_amdgcn_perm(0x41414141u, (v >> 1) & 0x1818u, 0x04010400u),
-                 __builtin_amdgcn_perm(0x41414141u, (v >> 3) & 0x1818u, 0x04010400u)};
+    // spread the 2-bit fields to nibbles
+    uint32_t u = (w0 & 0xFFu) | ((w0 & 0xFF00u) << 8);
+    u = (u & 0x000F000Fu) | ((u & 0x00F000F0u) << 4);
+    u = (u & 0x03030303u) | ((u & 0x0C0C0C0Cu) << 2);
+    return expand_nibbles(u ^ (sgn ? 0x22222222u : 0u));
   }
   // 8-bit: each code converted exactly to fp32, its upper half is the bf16
   const uint32_t a = w0 ^ (sgn ? 0x80808080u : 0u), b = w1 ^ (sgn ? 0x80808080u : 0u);
@@ -493,8 +481,11 @@ __device__ inline void mfma_acc(f32x4& P, const u32x4& a, const u32x4& b) {
                                               __builtin_bit_cast(bf16x8, b), P, 0, 0, 0);
 }
 
+typedef const void __attribute__((address_space(1)))* gvoid;
+typedef void __attribute__((address_space(3)))* lvoid;
+
 template <int BITS, bool SF16>
-__global__ __launch_bounds__(256) void dequant_gemm_kernel(
+__global__ __launch_bounds__(kGemmThreads) void dequant_gemm_kernel(
     const uint16_t* __restrict__ X, int64_t ldx, int64_t n,
     const uint32_t* __restrict__ qw, int64_t words,
     const void* __restrict__ scales, const uint8_t* __restrict__ zeros,
@@ -502,10 +493,10 @@ __global__ __launch_bounds__(256) void dequant_gemm_kernel(
     int sgn, void* __restrict__ Y, int64_t ldy, int out_bf16, int act, int vec,
     unsigned tiles_m, unsigned tiles) {
   constexpr int kSteps = kBk / 32;
-  constexpr int kUnits = kTm * kBk / 8 / 256;          // 8-column units per thread
-  __shared__ __attribute__((aligned(16))) uint16_t as[2][kTm][kAp];
+  __shared__ __attribute__((aligned(16))) char lA[2][kUnitsA * 16];
+  __shared__ __attribute__((aligned(16))) char lB[2][kUnitsB * 16];
   __shared__ int32_t gsh[2][kBk];
-  __shared__ __attribute__((aligned(16))) int32_t desc[2][kSteps];
+  __shared__ int32_t desc[2][kSteps];
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
   const int q = lane >> 4, c16 = lane & 15;
   // consecutive tiles share activation rows; spread them so that each
@@ -515,7 +506,10 @@ __global__ __launch_bounds__(256) void dequant_gemm_kernel(
   if (tile < 8 * per) tile = (tile % 8) * per + tile / 8;
   const int64_t rb = int64_t(tile % tiles_m) * kTn;     // first weight row
   const int64_t tb = int64_t(tile / tiles_m) * kTm;     // first activation row
-  const int wm = (wv & 1) * 64, wn = (wv >> 1) * 64;     // wave's offsets
+  const int wm = (wv & 3) * 64, wn = (wv >> 2) * 64;     // wave's offsets
+  // blocks whose activation rows all exist and lie 16-byte aligned go
+  // straight to LDS (the last, partial column block never does)
+  const bool direct_rows = (vec & kVecX) && tb + kTm <= n;
 
   // weight rows of the lane's B fragments (clamped; not stored past m)
   int64_t rowj[4];
@@ -531,17 +525,16 @@ __global__ __launch_bounds__(256) void dequant_gemm_kernel(
 #pragma unroll
     for (int j = 0; j < 4; ++j) acc[i][j] = P[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
   }
-  // the grid of the open group: 2 Delta (or Delta) and the zero term
+  // the grid of the open group: Delta and the zero term (16 + z, or z)
   float gs_s[4], gs_z[4];
   int cur = -1;        // open group (uniform over the workgroup), -1: none
 
   auto open_grid = [&](int G, float* s, float* z) {
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-      const float dl = load_scale<SF16>(scales, rowj[j] * ng + G);
+      s[j] = load_scale<SF16>(scales, rowj[j] * ng + G);
       const float zz = sgn ? zsgn : static_cast<float>(zeros[rowj[j] * ng + G]);
-      s[j] = kMagic ? 2.0f * dl : dl;
-      z[j] = kMagic ? 8.0f + 0.5f * zz : zz;
+      z[j] = kMagic ? 16.0f + zz : zz;
     }
   };
   // fold the group's products into the result, and clear them
@@ -559,23 +552,29 @@ __global__ __launch_bounds__(256) void dequant_gemm_kernel(
     }
   };
 
-  // ---- staging of one block's activations and group ids into registers
-  uint4 ax[kUnits];
-  int32_t gx = 0;
-  // a block whose activation rows all exist, 16-byte aligned and inside
-  // the input, stages with unconditional wide loads
-  const bool full_rows = (vec & kVecX) && tb + kTm <= n;
-  auto fetch = [&](int64_t c0) {
-    const bool wide = full_rows && c0 + kBk <= d;
+  // ---- activations of a block.  Direct: wave w's instruction i fills the
+  //      64 units of rows 8 (4 w + i) .. + 7, lane l writing slot l % 8 of
+  //      row l / 8, i.e. reading that row's unit (l % 8) ^ ((row / 2) % 8).
+  auto fetch_a_direct = [&](int64_t c0, int buf) {
 #pragma unroll
-    for (int h = 0; h < kUnits; ++h) {
-      const int u = tid + 256 * h;   // 8-column unit: row u / (kBk/8), run u % (kBk/8)
-      const int64_t tok = tb + u / (kBk / 8);
-      const int64_t cb = c0 + 8 * (u % (kBk / 8));
+    for (int i = 0; i < kUnitsA / 64 / 8; ++i) {
+      const int r = 8 * (4 * wv + i) + (lane >> 3);
+      const int c = (lane & 7) ^ ((r >> 1) & 7);
+      const uint16_t* src = X + (tb + r) * ldx + c0 + 8 * c;
+      __builtin_amdgcn_global_load_lds((gvoid)src,
+                                       (lvoid)(lA[buf] + (8 * (4 * wv + i)) * (kBk / 8) * 16),
+                                       16, 0, 0);
+    }
+  };
+  // through registers: thread t stages units t + 512 h (row u / 8, unit u % 8)
+  auto fetch_a_regs = [&](int64_t c0, int buf) {
+#pragma unroll
+    for (int h = 0; h < kUnitsA / kGemmThreads; ++h) {
+      const int u = tid + kGemmThreads * h;
+      const int r = u >> 3, c = u & 7;
+      const int64_t tok = tb + r, cb = c0 + 8 * c;
       uint4 v = uint4{0u, 0u, 0u, 0u};
-      if (wide) {
-        v = *reinterpret_cast<const uint4*>(X + tok * ldx + cb);
-      } else if (tok < n) {
+      if (tok < n) {
         const uint16_t* src = X + tok * ldx + cb;
         if ((vec & kVecX) && cb + 8 <= d) {
           v = *reinterpret_cast<const uint4*>(src);
@@ -587,19 +586,28 @@ __global__ __launch_bounds__(256) void dequant_gemm_kernel(
                     e[6] | (e[7] << 16)};
         }
       }
-      ax[h] = stage_order<BITS>(v);
+      *reinterpret_cast<uint4*>(lA[buf] + unit_off(r, c)) = v;
     }
+  };
+  // ---- codes and group ids of a block (registers): thread t takes runs
+  //      2 (t % 4), + 1 of weight row t / 4
+  const int brow = tid >> 2, bc = 2 * (tid & 3);
+  const uint32_t* bsrc = qw + min<int64_t>(rb + brow, m - 1) * words;
+  uint32_t cw[2][2];
+  int32_t gx = 0;
+  auto fetch_codes = [&](int64_t c0) {
+#pragma unroll
+    for (int e = 0; e < 2; ++e) load_run<BITS>(bsrc, words, c0 / 8 + bc + e, cw[e][0], cw[e][1]);
     if (tid < kBk) gx = g_idx[min<int64_t>(c0 + tid, d - 1)];
   };
-  // LDS writes of the staged block; the waves holding group ids also write
-  // one descriptor per 32-column step: its group when all its columns share
+  // expanded codes to LDS; the lanes holding group ids also write one
+  // descriptor per 32-column step: its group when all its columns share
   // one, else -1
-  auto store = [&](int buf) {
+  auto store_codes = [&](int buf) {
 #pragma unroll
-    for (int h = 0; h < kUnits; ++h) {
-      const int u = tid + 256 * h;
-      *reinterpret_cast<uint4*>(&as[buf][u / (kBk / 8)][8 * (u % (kBk / 8))]) = ax[h];
-    }
+    for (int e = 0; e < 2; ++e)
+      *reinterpret_cast<u32x4*>(lB[buf] + unit_off(brow, bc + e)) =
+          expand_run<BITS>(cw[e][0], cw[e][1], sgn);
     if (tid < kBk) {
       gsh[buf][tid] = gx;
       const int half = lane & 32;
@@ -609,60 +617,42 @@ __global__ __launch_bounds__(256) void dequant_gemm_kernel(
         desc[buf][tid >> 5] = ((same >> half) & 0xFFFFFFFFull) == 0xFFFFFFFFull ? G0 : -1;
     }
   };
-  // codes of the lane's runs in the steps of a block
-  uint32_t cw[kSteps][4][2];
-  auto fetch_codes = [&](int64_t c0) {
-#pragma unroll
-    for (int s = 0; s < kSteps; ++s)
-#pragma unroll
-      for (int j = 0; j < 4; ++j)
-        load_run<BITS>(qw + rowj[j] * words, words, (c0 + 32 * s) / 8 + q, cw[s][j][0],
-                       cw[s][j][1]);
-  };
-  auto read_a = [&](int buf, int s, u32x4* A) {
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-      A[i] = *reinterpret_cast<const u32x4*>(&as[buf][wm + 16 * i + c16][32 * s + 8 * q]);
+  auto fetch_a = [&](int64_t c0, int buf) {
+    if (direct_rows && c0 + kBk <= d) fetch_a_direct(c0, buf);
+    else fetch_a_regs(c0, buf);
   };
 
   const int64_t nblk = (d + kBk - 1) / kBk;
-  fetch(0);
+  fetch_a(0, 0);
   fetch_codes(0);
-  store(0);
+  store_codes(0);
+  __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
   const u32x4 ones = u32x4{0x3F803F80u, 0x3F803F80u, 0x3F803F80u, 0x3F803F80u};
   for (int64_t blk = 0; blk < nblk; ++blk) {
     const int buf = static_cast<int>(blk & 1);
     const int64_t c0 = blk * kBk;
-    int dsc[kSteps];
-#pragma unroll
-    for (int s = 0; s < kSteps; ++s) dsc[s] = __builtin_amdgcn_readfirstlane(desc[buf][s]);
-    u32x4 An[4];
-    read_a(buf, 0, An);
-    uint32_t cc[kSteps][4][2];
-#pragma unroll
-    for (int s = 0; s < kSteps; ++s)
-#pragma unroll
-      for (int j = 0; j < 4; ++j) { cc[s][j][0] = cw[s][j][0]; cc[s][j][1] = cw[s][j][1]; }
-    if (blk + 1 < nblk) {
-      fetch(c0 + kBk);
+    const bool more = blk + 1 < nblk;
+    if (more) {
+      fetch_a(c0 + kBk, buf ^ 1);
       fetch_codes(c0 + kBk);
     }
 #pragma unroll
     for (int s = 0; s < kSteps; ++s) {
       if (c0 + 32 * s >= d) break;       // steps past the end of the input
-      u32x4 A[4];
+      const int cs = 4 * s + q;          // the lane's unit within the block
+      u32x4 A[4], B[4];
 #pragma unroll
-      for (int i = 0; i < 4; ++i) A[i] = An[i];
-      if (s + 1 < kSteps) read_a(buf, s + 1, An);    // next step's fragments
-      u32x4 B[4];
+      for (int i = 0; i < 4; ++i)
+        A[i] = *reinterpret_cast<const u32x4*>(lA[buf] + unit_off(wm + 16 * i + c16, cs));
 #pragma unroll
-      for (int j = 0; j < 4; ++j) B[j] = expand_codes<BITS>(cc[s][j][0], cc[s][j][1], sgn);
+      for (int j = 0; j < 4; ++j)
+        B[j] = *reinterpret_cast<const u32x4*>(lB[buf] + unit_off(wn + 16 * j + c16, cs));
       // the groups present among the step's 32 columns, one pass each in
       // the order of their first column (one pass when the descriptor names
       // the step's single group); a pass masks the activations of the other
       // groups' columns (lane l of the group-id read: column l % 32)
-      const int Gs = dsc[s];
+      const int Gs = __builtin_amdgcn_readfirstlane(desc[buf][s]);
       int gl = Gs;
       if (Gs < 0) gl = gsh[buf][32 * s + (lane & 31)];
       uint64_t left = 0xFFFFFFFFull;
@@ -680,9 +670,9 @@ __global__ __launch_bounds__(256) void dequant_gemm_kernel(
         if (in != 0xFFFFFFFFull) {
 #pragma unroll
           for (int p = 0; p < 4; ++p) {
-            const int e0 = 32 * s + 8 * q + run_col<BITS>(2 * p);
-            const int e1 = 32 * s + 8 * q + run_col<BITS>(2 * p + 1);
-            mk[p] = (gsh[buf][e0] == G ? 0x0000FFFFu : 0u) | (gsh[buf][e1] == G ? 0xFFFF0000u : 0u);
+            const int e0 = 32 * s + 8 * q + 2 * p;
+            mk[p] = (gsh[buf][e0] == G ? 0x0000FFFFu : 0u) |
+                    (gsh[buf][e0 + 1] == G ? 0xFFFF0000u : 0u);
           }
         }
 #pragma unroll
@@ -696,7 +686,9 @@ __global__ __launch_bounds__(256) void dequant_gemm_kernel(
         }
       } while (left);
     }
-    if (blk + 1 < nblk) store(buf ^ 1);
+    if (more) store_codes(buf ^ 1);
+    // the next block's direct loads have landed before anyone reads them
+    __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
   }
   if (cur >= 0) fold(gs_s, gs_z);
@@ -734,7 +726,7 @@ gptq_status launch_bits(const uint16_t* X, int64_t ldx, int64_t n, const uint32_
   if (n > 16) {
     const unsigned tiles_m = cdiv(m, kTn);
     const unsigned tiles = tiles_m * cdiv(n, kTm);
-    dequant_gemm_kernel<BITS, SF16><<<tiles, 256, 0, st>>>(
+    dequant_gemm_kernel<BITS, SF16><<<tiles, kGemmThreads, 0, st>>>(
         X, ldx, n, qw, words, scales, zeros, ng, g_idx, m, d, sgn, Y, ldy, out_bf16, act, vecx,
         tiles_m, tiles);
     GPTQ_CHECK_LAUNCH();
