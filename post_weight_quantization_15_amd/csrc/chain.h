@@ -112,20 +112,31 @@ __device__ inline void row_minmax(float& lo, float& hi) {
 // The quotients w / Delta and rho / R_jj are products with fp32
 // reciprocals; they differ from the IEEE quotients by at most an ulp, which
 // can only matter within 1e-6 of a rounding boundary.
+// nblk > 1 (full blocks of one lazy batch, VEC == 2): the launch runs the
+// blocks i0, i0 + bi, ... one after the other for its rows; block u first
+// takes the residuals of the blocks before it in the batch (rows are
+// independent, so they are this workgroup's own, written by it to E and read
+// back after a barrier).
 template <int FS, int VEC, bool EXACT>
 __global__ __launch_bounds__(256) void chain_kernel(
     const float* __restrict__ WT, int64_t m, int64_t d, const float* __restrict__ RL,
-    int64_t i0, int bw_arg, int bi, float maxq, int64_t gsize, int sym, int sgn,
+    int64_t i0_arg, int bw_arg, int bi, float maxq, int64_t gsize, int sym, int sgn,
     int cmask, const int32_t* __restrict__ perm,
     float* __restrict__ scalesP, uint8_t* __restrict__ zerosP,
-    uint8_t* __restrict__ codesP, float* __restrict__ E,
-    const float* __restrict__ R, int64_t sb0, int kn, const float* __restrict__ Esb) {
+    uint8_t* __restrict__ codesP, float* __restrict__ E_arg,
+    const float* __restrict__ R, int64_t sb0, int kn_arg, const float* __restrict__ Esb,
+    int nblk) {
   const int bw = VEC == 2 ? kB : bw_arg;
   constexpr int kSg = FS == kFsStatic ? kB : 1;
   __shared__ __attribute__((aligned(16))) float rl[kB * kB];
   __shared__ float tile[kB][kTp];
   __shared__ __attribute__((aligned(16))) uint8_t ctile[kB][kChainRows];
   __shared__ float sgs[kSg][kChainRows], sgz[kSg][kChainRows], sgi[kSg][kChainRows];
+  for (int blk = 0; blk < nblk; ++blk) {
+  const int64_t i0 = i0_arg + int64_t(blk) * bi;
+  const int kn = kn_arg + blk * bi;
+  float* __restrict__ E = E_arg + int64_t(blk) * bi * m;
+  if (blk > 0) __syncthreads();   // the previous block's reads of rl / tile / ctile
   const int tid = threadIdx.x;
   const int rr = tid >> 4, q = tid & 15;
   const int64_t r0 = int64_t(blockIdx.x) * kChainRows;
@@ -375,15 +386,14 @@ __global__ __launch_bounds__(256) void chain_kernel(
         }
     }
   }
+  }
 }
 
 // Launches chain_kernel<FS, VEC, EXACT> for the VEC and EXACT the
 // arguments allow.
 template <int FS>
 gptq_status launch_fs(const ChainArgs& a, hipStream_t st) {
-  const bool vec = a.m % 4 == 0 && reinterpret_cast<uintptr_t>(a.WT) % 16 == 0 &&
-                   reinterpret_cast<uintptr_t>(a.E) % 16 == 0 &&
-                   reinterpret_cast<uintptr_t>(a.codesP) % 4 == 0;
+  const bool vec = chain_vec(a);
   const dim3 grid(static_cast<unsigned>((a.m + kChainRows - 1) / kChainRows));
   // groups of exactly FS columns starting on an FS boundary: every FS-th
   // block column starts a group, known at compile time (the fits are then
@@ -392,7 +402,9 @@ gptq_status launch_fs(const ChainArgs& a, hipStream_t st) {
 #define GPTQ_CHAIN(V, X)                                                         \
   chain_kernel<FS, V, X><<<grid, 256, 0, st>>>(                                   \
       a.WT, a.m, a.d, a.RL, a.i0, a.bw, a.bi, a.maxq, a.gsize, a.sym, a.sgn,     \
-      a.cmask, a.perm, a.scalesP, a.zerosP, a.codesP, a.E, a.R, a.sb0, a.kn, a.Esb)
+      a.cmask, a.perm, a.scalesP, a.zerosP, a.codesP, a.E, a.R, a.sb0, a.kn, a.Esb, \
+      a.nblk)
+  if (a.nblk > 1 && !(vec && a.bw == kB)) return GPTQ_ERR_INVALID_ARG;
   if (vec && a.bw == kB) {
     if constexpr (FS > 0) {
       if (exact)

@@ -131,7 +131,14 @@ struct ChainArgs {
   int64_t sb0;
   int kn;
   const float* Esb;
+  int nblk = 1;        // full blocks i0, i0 + bi, ... run by one launch (1 or 2)
 };
+// The chain's 16-byte global accesses need these alignments.
+inline bool chain_vec(const ChainArgs& a) {
+  return a.m % 4 == 0 && reinterpret_cast<uintptr_t>(a.WT) % 16 == 0 &&
+         reinterpret_cast<uintptr_t>(a.E) % 16 == 0 &&
+         reinterpret_cast<uintptr_t>(a.codesP) % 4 == 0;
+}
 gptq_status launch_chain(const ChainArgs& a, hipStream_t st);
 // per-variant launchers (one instantiation unit each)
 gptq_status launch_chain_row(const ChainArgs& a, hipStream_t st);

@@ -245,15 +245,23 @@ gptq_status enqueue_columns(const void* W, gptq_dtype w_dtype, int64_t m,
   a.Esb = q.E;
   for (int64_t s0 = 0; s0 < d; s0 += int64_t(nb) * bi) {
     int64_t i0 = s0;
+    // a batch of full blocks runs in one launch (rows are independent, so
+    // each workgroup carries its rows through the batch's blocks in turn)
+    a.i0 = s0;
+    a.E = q.E;
+    a.bw = bi;
+    const bool one_launch = nb > 1 && s0 + int64_t(nb) * bi <= d && chain_vec(a);
     for (int j = 0; j < nb && i0 < d; ++j, i0 += bi) {
       a.i0 = i0;
       a.bw = static_cast<int>(std::min<int64_t>(bi, d - i0));
       a.E = q.E + (i0 - s0) * m;
       a.sb0 = s0;
       a.kn = static_cast<int>(i0 - s0);
+      a.nblk = one_launch ? nb : 1;
       tk = trace_begin(st, GPTQ_TRACE_CHAIN);
       if ((s = launch_chain(a, st)) != GPTQ_OK) return s;
       trace_end(st, tk);
+      if (one_launch) break;
     }
     const int kw = static_cast<int>(std::min<int64_t>(int64_t(nb) * bi, d - s0));
     if (d - s0 - kw > 0) {

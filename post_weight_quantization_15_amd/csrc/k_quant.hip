@@ -128,32 +128,38 @@ __global__ void zero_fill_kernel(float* __restrict__ p, int64_t n) {
 }
 
 // WT[i2 + t][r] -= sum_k R[i0 + k][i2 + t] * E[k][r]   (t < d - i2, r < m).
-// 256 threads = 2 x 2 waves, each a 64 (t) x 64 (r) tile of 4 x 4
-// 16x16x4 MFMA blocks.  Lane l feeds A[row = l%16][k = l/16] and
-// B[k = l/16][col = l%16] and receives D[row = 4(l/16) + v][col = l%16].
-// Block a of a wave covers t = tw + a + 4 row, block b covers
-// r = rw + b + 4 col, so a lane's four blocks touch four consecutive t (or r):
-// operands arrive as one 16-byte load per k step and the final
-// read-modify-write of W is one 16-byte access per (a, v).  Operands are
-// prefetched kDepth k steps ahead in a register ring; the W values to update
-// are loaded before the product starts.
+// 256 threads = 2 x 2 waves, each a (16 NA) (t) x 64 (r) tile of NA x 4
+// 16x16x4 MFMA blocks (NA = 4 or 2).  Lane l feeds A[row = l%16][k = l/16]
+// and B[k = l/16][col = l%16] and receives D[row = 4(l/16) + v][col = l%16].
+// Block a of a wave covers t = tw + a + NA row, block b covers
+// r = rw + b + 4 col, so a lane's blocks touch NA consecutive t (or four
+// consecutive r): operands arrive as one 8- or 16-byte load per k step and
+// the final read-modify-write of W is one 16-byte access per (a, v).
+// Operands are prefetched kDepth k steps ahead in a register ring; the W
+// values to update are loaded before the product starts.  The narrow form
+// (NA = 2) doubles the workgroups of a launch, for launches whose wide
+// workgroups would leave part of the chip idle in their last round.
 constexpr int kDepth = 4;
 
-// Elements c0..c0+3 of a row, the address clamped into [0, lim).  Lanes
+// Elements c0..c0+N-1 of a row, the address clamped into [0, lim).  Lanes
 // whose columns fall past lim only feed outputs that are never stored, so
 // the data needs no masking (a select on loaded data would pin the wait for
-// the load next to the load).
-template <bool VEC>
+// the load next to the load).  Elements N..3 of the result are unused.
+template <bool VEC, int N>
 __device__ inline f32x4 load4(const float* row, int64_t c0, int64_t lim) {
-  if (VEC)     // lim, c0 multiples of 4 (lim >= 4), row 16-byte aligned
-    return *reinterpret_cast<const f32x4*>(row + (c0 < lim ? c0 : lim - 4));
-  f32x4 v;
+  if (VEC) {   // lim, c0 multiples of 4 (lim >= 4), row 16-byte aligned
+    const float* p = row + (c0 < lim ? c0 : lim - N);
+    if (N == 4) return *reinterpret_cast<const f32x4*>(p);
+    const float2 v = *reinterpret_cast<const float2*>(p);
+    return f32x4{v.x, v.y, 0.f, 0.f};
+  }
+  f32x4 v = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-  for (int c = 0; c < 4; ++c) v[c] = row[min(c0 + c, lim - 1)];
+  for (int c = 0; c < N; ++c) v[c] = row[min(c0 + c, lim - 1)];
   return v;
 }
 
-template <bool VEC, int KS>
+template <bool VEC, int KS, int NA>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2)))
 void lazy_update_kernel(
     float* __restrict__ WT, int64_t m, int64_t d, const float* __restrict__ R,
@@ -161,32 +167,32 @@ void lazy_update_kernel(
   const int64_t i2 = i0 + bw, nT = d - i2;
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int lr = lane & 15, lk = lane >> 4;
-  const int64_t tw = int64_t(blockIdx.y) * 128 + (wave >> 1) * 64;
+  const int64_t tw = int64_t(blockIdx.y) * (32 * NA) + (wave >> 1) * (16 * NA);
   const int64_t rw = int64_t(blockIdx.x) * 128 + (wave & 1) * 64;
-  const int64_t ta = tw + 4 * lr, rb = rw + 4 * lr;
+  const int64_t ta = tw + NA * lr, rb = rw + 4 * lr;
   const float* Rt = R + i0 * d + i2;       // Rt[k d + t]
   auto ldA = [&](int ks) -> f32x4 {
     const int k = 4 * ks + lk;
-    return load4<VEC>(Rt + int64_t(min(k, bw - 1)) * d, ta, nT);
+    return load4<VEC, NA>(Rt + int64_t(min(k, bw - 1)) * d, ta, nT);
   };
   auto ldB = [&](int ks) -> f32x4 {
     const int k = 4 * ks + lk;
-    return load4<VEC>(E + int64_t(k) * m, rb, m);     // rows >= bw are zero
+    return load4<VEC, 4>(E + int64_t(k) * m, rb, m);     // rows >= bw are zero
   };
-  f32x4 Wv[4][4];
+  f32x4 Wv[NA][4];
   auto ldW = [&]() {
 #pragma unroll
-    for (int a = 0; a < 4; ++a)
+    for (int a = 0; a < NA; ++a)
 #pragma unroll
       for (int v = 0; v < 4; ++v) {
-        const int64_t t = tw + a + 16 * lk + 4 * v;
-        Wv[a][v] = load4<VEC>(WT + (i2 + min(t, nT - 1)) * m, rb, m);
+        const int64_t t = tw + a + 4 * NA * lk + NA * v;
+        Wv[a][v] = load4<VEC, 4>(WT + (i2 + min(t, nT - 1)) * m, rb, m);
       }
   };
   constexpr int kWAt = KS > 8 ? KS - 8 : 0;   // step after which W is fetched
-  f32x4 acc[4][4];
+  f32x4 acc[NA][4];
 #pragma unroll
-  for (int a = 0; a < 4; ++a)
+  for (int a = 0; a < NA; ++a)
 #pragma unroll
     for (int b = 0; b < 4; ++b) acc[a][b] = f32x4{0.f, 0.f, 0.f, 0.f};
   // KS k steps (4 k each) cover bw, fully unrolled; rows bw..4 KS - 1 of E
@@ -203,7 +209,7 @@ void lazy_update_kernel(
   for (int ks = 0; ks < KS; ++ks) {
     const int s = ks % kDepth;
 #pragma unroll
-    for (int a = 0; a < 4; ++a)
+    for (int a = 0; a < NA; ++a)
 #pragma unroll
       for (int b = 0; b < 4; ++b)
         acc[a][b] = __builtin_amdgcn_mfma_f32_16x16x4f32(A[s][a], B[s][b], acc[a][b], 0, 0, 0);
@@ -215,10 +221,10 @@ void lazy_update_kernel(
     __builtin_amdgcn_sched_barrier(0);
   }
 #pragma unroll
-  for (int a = 0; a < 4; ++a)
+  for (int a = 0; a < NA; ++a)
 #pragma unroll
     for (int v = 0; v < 4; ++v) {
-      const int64_t t = tw + a + 16 * lk + 4 * v;
+      const int64_t t = tw + a + 4 * NA * lk + NA * v;
       if (t >= nT) continue;
       f32x4 x = Wv[a][v];
 #pragma unroll
@@ -235,6 +241,15 @@ void lazy_update_kernel(
 }
 
 unsigned cdiv(int64_t a, int64_t b) { return static_cast<unsigned>((a + b - 1) / b); }
+
+template <bool VEC, int KS>
+void lazy_launch(bool narrow, dim3 grid, hipStream_t st, float* WT, int64_t m,
+                 int64_t d, const float* R, int64_t i0, int bw, const float* E) {
+  if (narrow)
+    lazy_update_kernel<VEC, KS, 2><<<grid, 256, 0, st>>>(WT, m, d, R, i0, bw, E);
+  else
+    lazy_update_kernel<VEC, KS, 4><<<grid, 256, 0, st>>>(WT, m, d, R, i0, bw, E);
+}
 
 }  // namespace
 
@@ -299,7 +314,16 @@ gptq_status launch_lazy_update(float* WT, int64_t m, int64_t d, const float* R,
                                hipStream_t st) {
   const int64_t nT = d - i0 - bw;
   if (nT <= 0) return GPTQ_OK;
-  const dim3 grid(cdiv(m, 128), cdiv(nT, 128));
+  // Workgroups run one per CU at a time here, each for a time about
+  // proportional to its tile; the narrow tile (half the work, a little less
+  // efficient per product) is taken when its rounds of kCUs workgroups come
+  // out shorter.
+  constexpr int64_t kCUs = 256;
+  const int64_t wg_wide = int64_t(cdiv(m, 128)) * cdiv(nT, 128);
+  const int64_t wg_narrow = int64_t(cdiv(m, 128)) * cdiv(nT, 64);
+  const bool narrow = 0.6 * double((wg_narrow + kCUs - 1) / kCUs) <
+                      double((wg_wide + kCUs - 1) / kCUs);
+  const dim3 grid(cdiv(m, 128), cdiv(nT, narrow ? 64 : 128));
   // 16-byte accesses need every row start and column offset 4-aligned
   const bool vec = m % 4 == 0 && d % 4 == 0 && (i0 + bw) % 4 == 0 &&
                    reinterpret_cast<uintptr_t>(R) % 16 == 0 &&
@@ -311,7 +335,7 @@ gptq_status launch_lazy_update(float* WT, int64_t m, int64_t d, const float* R,
     const int64_t n = int64_t(kpad - bw) * m;
     zero_fill_kernel<<<cdiv(n, 256), 256, 0, st>>>(E + int64_t(bw) * m, n);
   }
-#define GPTQ_LAZY(V, K) lazy_update_kernel<V, K><<<grid, 256, 0, st>>>(WT, m, d, R, i0, bw, E)
+#define GPTQ_LAZY(V, K) lazy_launch<V, K>(narrow, grid, st, WT, m, d, R, i0, bw, E)
 #define GPTQ_LAZY_KS(V)                        \
   if (ks <= 4) GPTQ_LAZY(V, 4);                 \
   else if (ks <= 8) GPTQ_LAZY(V, 8);            \
