@@ -48,7 +48,7 @@ gptq_status scratch_address(hipStream_t st, void** out) {
 
 constexpr int64_t kMaxDim = 65535;   // grid.y limit of the per-row launches
 constexpr int kChainMaxBlock = 128;
-constexpr int kLazyBatch = 2;        // chain blocks per lazy (far) update
+constexpr int kLazyBatch = 4;        // chain blocks per lazy (far) update
 constexpr int kMaxRetries = 5;
 
 bool valid_dtype(gptq_dtype t) { return t == GPTQ_BF16 || t == GPTQ_F32; }
