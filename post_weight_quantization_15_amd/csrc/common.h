@@ -77,7 +77,7 @@ gptq_status launch_prep_stats(const float* S, int64_t d, int64_t n,
 gptq_status launch_perm(int64_t d, int act_order, const FactorWs& f,
                         int32_t* perm, hipStream_t st);
 gptq_status launch_build_h(const float* S, int64_t d, int64_t n,
-                           const int32_t* perm, const uint8_t* dead,
+                           const int32_t* perm, const uint8_t* dead, bool ident,
                            const FactorWs& f, hipStream_t st);
 // U (in H) and R = U^-1 (in R), the inverse partly beside the factor on a
 // second stream; the caller's stream has waited for it on return.

@@ -150,7 +150,7 @@ gptq_status enqueue_factor(const float* S, int64_t n, int64_t d, float percdamp,
   const int tk = trace_begin(st, GPTQ_TRACE_FACTOR);
   if ((s = launch_prep_stats(S, d, n, percdamp, attempt, f, dead, st)) != GPTQ_OK) return s;
   if (attempt == 0 && (s = launch_perm(d, act_order, f, perm, st)) != GPTQ_OK) return s;
-  if ((s = launch_build_h(S, d, n, perm, dead, f, st)) != GPTQ_OK) return s;
+  if ((s = launch_build_h(S, d, n, perm, dead, act_order == 0, f, st)) != GPTQ_OK) return s;
   if ((s = launch_factor_inverse(d, f, st)) != GPTQ_OK) return s;
   s = launch_r_to_f32(d, f, R, st);
   trace_end(st, tk);

@@ -108,24 +108,35 @@ __global__ void identity_perm_kernel(int64_t d, int32_t* __restrict__ perm) {
 }
 
 // H[a][b] = (2/n) S[perm a][perm b] (+ damp on the diagonal; dead diagonal
-// entries are 1 before damping).  Upper triangle only.
+// entries are 1 before damping).  Upper triangle only: one workgroup per
+// row a, its threads taking the columns b >= a, four per pass (independent
+// loads in flight); ident: perm is the identity (no gather of perm[b]).
 __global__ __launch_bounds__(256) void build_h_kernel(
     const float* __restrict__ S, int64_t d, int64_t n,
     const int32_t* __restrict__ perm, const uint8_t* __restrict__ dead,
-    const double* __restrict__ damp, double* __restrict__ H) {
-  const int64_t a = blockIdx.y;
-  const int64_t b = int64_t(blockIdx.x) * 256 + threadIdx.x;
-  if (b >= d || b < a) return;
+    const double* __restrict__ damp, int ident, double* __restrict__ H) {
+  const int64_t a = blockIdx.x;
   const double scale = 2.0 / double(n);
-  const int64_t pa = perm[a];
-  double h;
-  if (a == b) {
-    h = dead[pa] ? 1.0 : scale * double(S[pa * d + pa]);
-    h += *damp;
-  } else {
-    h = scale * double(S[pa * d + perm[b]]);
+  const int64_t pa = ident ? a : perm[a];
+  const float* Srow = S + pa * d;
+  double* Hrow = H + a * d;
+  const int64_t b0 = (a & ~int64_t(255)) + threadIdx.x;
+  for (int64_t bb = b0; bb < d; bb += 1024) {
+    float v[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int64_t b = bb + 256 * u;
+      v[u] = (b >= a && b < d) ? Srow[ident ? b : perm[b]] : 0.0f;
+    }
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int64_t b = bb + 256 * u;
+      if (b < a || b >= d) continue;
+      double h = scale * double(v[u]);
+      if (b == a) h = (dead[pa] ? 1.0 : h) + *damp;
+      Hrow[b] = h;
+    }
   }
-  H[a * d + b] = h;
 }
 
 // ---------------------------------------------------------------------------
@@ -801,12 +812,26 @@ __global__ __launch_bounds__(256) void trtri_r_kernel(
   }
 }
 
+// fp32 copy of R with its lower triangle zeroed: one workgroup per row,
+// four columns per thread and pass.
 __global__ __launch_bounds__(256) void r_to_f32_kernel(
     const double* __restrict__ R64, int64_t d, float* __restrict__ R) {
-  const int64_t a = blockIdx.y;
-  const int64_t b = int64_t(blockIdx.x) * 256 + threadIdx.x;
-  if (b >= d) return;
-  R[a * d + b] = (b >= a) ? static_cast<float>(R64[a * d + b]) : 0.0f;
+  const int64_t a = blockIdx.x;
+  const double* src = R64 + a * d;
+  float* dst = R + a * d;
+  for (int64_t bb = threadIdx.x; bb < d; bb += 1024) {
+    float v[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int64_t b = bb + 256 * u;
+      v[u] = (b >= a && b < d) ? static_cast<float>(src[b]) : 0.0f;
+    }
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int64_t b = bb + 256 * u;
+      if (b < d) dst[b] = v[u];
+    }
+  }
 }
 
 unsigned cdiv(int64_t a, int64_t b) { return static_cast<unsigned>((a + b - 1) / b); }
@@ -857,10 +882,10 @@ gptq_status launch_perm(int64_t d, int act_order, const FactorWs& f,
 }
 
 gptq_status launch_build_h(const float* S, int64_t d, int64_t n,
-                           const int32_t* perm, const uint8_t* dead,
+                           const int32_t* perm, const uint8_t* dead, bool ident,
                            const FactorWs& f, hipStream_t st) {
-  build_h_kernel<<<dim3(cdiv(d, 256), static_cast<unsigned>(d)), 256, 0, st>>>(
-      S, d, n, perm, dead, f.damp, f.H);
+  build_h_kernel<<<static_cast<unsigned>(d), 256, 0, st>>>(S, d, n, perm, dead, f.damp,
+                                                           ident ? 1 : 0, f.H);
   GPTQ_CHECK_LAUNCH();
   return GPTQ_OK;
 }
@@ -1090,7 +1115,7 @@ gptq_status launch_factor_inverse(int64_t d, const FactorWs& f, hipStream_t st) 
 
 gptq_status launch_r_to_f32(int64_t d, const FactorWs& f, float* R,
                             hipStream_t st) {
-  r_to_f32_kernel<<<dim3(cdiv(d, 256), static_cast<unsigned>(d)), 256, 0, st>>>(f.R, d, R);
+  r_to_f32_kernel<<<static_cast<unsigned>(d), 256, 0, st>>>(f.R, d, R);
   GPTQ_CHECK_LAUNCH();
   return GPTQ_OK;
 }
