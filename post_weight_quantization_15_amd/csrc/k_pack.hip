@@ -11,41 +11,63 @@
 namespace gptq {
 namespace {
 
-// codesO[r][c] = codesP[pinv[c]][r] through 64x64 LDS tiles.
-__global__ __launch_bounds__(256) void unpermute_codes_kernel(
+// One 64-row x 64-column tile of the outputs: the codes of original columns
+// c0..c0+63 (processing positions pinv[c]) gathered through LDS, then
+// packed: a row's 64 b-bit codes are exactly 2b words of its bit stream
+// (the tile starts on bit 64 b c0 / 64, a word boundary).  codesO[r][c]
+// (the unpacked codes in original order) is written as well when given.
+// VEC: m % 4 == 0 and codesP 4-byte aligned, four rows per load.
+template <bool VEC>
+__global__ __launch_bounds__(256) void unpermute_pack_kernel(
     const uint8_t* __restrict__ codesP, int64_t m, int64_t d,
-    const int32_t* __restrict__ pinv, uint8_t* __restrict__ codesO) {
-  __shared__ uint8_t tile[64][65];
+    const int32_t* __restrict__ pinv, int bits, int64_t words,
+    uint32_t* __restrict__ qweight, uint8_t* __restrict__ codesO) {
+  __shared__ __attribute__((aligned(16))) uint8_t tile[64][68];   // [column][row]
   const int64_t r0 = int64_t(blockIdx.x) * 64, c0 = int64_t(blockIdx.y) * 64;
-  const int lx = threadIdx.x & 63, ly = threadIdx.x >> 6;
-  for (int y = ly; y < 64; y += 4) {
-    const int64_t c = c0 + y, r = r0 + lx;
-    tile[y][lx] = (c < d && r < m) ? codesP[int64_t(pinv[c]) * m + r] : 0;
+  const int t = threadIdx.x;
+  if (VEC) {
+    const int q = t & 15;
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      const int y = (t >> 4) + 16 * k;
+      const int64_t c = c0 + y, r = r0 + 4 * q;
+      uint32_t v = 0;
+      if (c < d && r < m) v = *reinterpret_cast<const uint32_t*>(codesP + int64_t(pinv[c]) * m + r);
+      *reinterpret_cast<uint32_t*>(&tile[y][4 * q]) = v;
+    }
+  } else {
+    const int lx = t & 63, ly = t >> 6;
+    for (int y = ly; y < 64; y += 4) {
+      const int64_t c = c0 + y, r = r0 + lx;
+      tile[y][lx] = (c < d && r < m) ? codesP[int64_t(pinv[c]) * m + r] : 0;
+    }
   }
   __syncthreads();
-  for (int y = ly; y < 64; y += 4) {
-    const int64_t r = r0 + y, c = c0 + lx;
-    if (r < m && c < d) codesO[r * d + c] = tile[lx][y];
+  // thread (row rr, word slot ws): words ws, ws + 4, ... of the row's 2b
+  const int rr = t >> 2, ws = t & 3;
+  const int64_t r = r0 + rr;
+  if (r < m) {
+    const int64_t w0 = c0 * bits / 32;
+    for (int w = ws; w < 2 * bits; w += 4) {
+      if (w0 + w >= words) break;
+      const int bit0 = 32 * w;
+      const int cfirst = bit0 / bits, clast = min((bit0 + 31) / bits, 63);
+      uint32_t word = 0;
+      for (int c = cfirst; c <= clast; ++c) {
+        const int sh = c * bits - bit0;
+        const uint32_t code = tile[c][rr];
+        word |= (sh >= 0) ? (code << sh) : (code >> (-sh));
+      }
+      qweight[r * words + w0 + w] = word;
+    }
   }
-}
-
-__global__ __launch_bounds__(256) void pack_kernel(
-    const uint8_t* __restrict__ codesO, int64_t m, int64_t d, int bits,
-    int64_t words, uint32_t* __restrict__ qweight) {
-  const int64_t w = int64_t(blockIdx.x) * 256 + threadIdx.x;
-  const int64_t r = blockIdx.y;
-  if (w >= words) return;
-  const int64_t bit0 = 32 * w;
-  const int64_t cfirst = bit0 / bits;
-  const int64_t clast = min((bit0 + 31) / bits, d - 1);
-  const uint8_t* row = codesO + r * d;
-  uint32_t word = 0;
-  for (int64_t c = cfirst; c <= clast; ++c) {
-    const int64_t sh = c * bits - bit0;
-    const uint32_t code = row[c];
-    word |= (sh >= 0) ? (code << sh) : (code >> (-sh));
+  if (codesO) {
+    const int lx = t & 63, ly = t >> 6;
+    for (int y = ly; y < 64; y += 4) {
+      const int64_t rrow = r0 + y, c = c0 + lx;
+      if (rrow < m && c < d) codesO[rrow * d + c] = tile[lx][y];
+    }
   }
-  qweight[r * words + w] = word;
 }
 
 // scales[r][g] = scalesP[g][r], zeros likewise (0 for signed codes: their
@@ -101,9 +123,13 @@ gptq_status launch_outputs(int64_t m, int64_t d, int bits, int gsize, int sgn,
                            int32_t* g_idx, float* w_hat, hipStream_t st) {
   const int64_t ng = gsize > 0 ? (d + gsize - 1) / gsize : 1;
   const int64_t words = (d * bits + 31) / 32;
-  unpermute_codes_kernel<<<dim3(cdiv(m, 64), cdiv(d, 64)), 256, 0, st>>>(codesP, m, d, pinv, codesO);
-  GPTQ_CHECK_LAUNCH();
-  pack_kernel<<<dim3(cdiv(words, 256), static_cast<unsigned>(m)), 256, 0, st>>>(codesO, m, d, bits, words, qweight);
+  // the unpacked codes in original order are kept only for w_hat
+  uint8_t* co = w_hat ? codesO : nullptr;
+  const dim3 grid(cdiv(m, 64), cdiv(d, 64));
+  if (m % 4 == 0 && reinterpret_cast<uintptr_t>(codesP) % 4 == 0)
+    unpermute_pack_kernel<true><<<grid, 256, 0, st>>>(codesP, m, d, pinv, bits, words, qweight, co);
+  else
+    unpermute_pack_kernel<false><<<grid, 256, 0, st>>>(codesP, m, d, pinv, bits, words, qweight, co);
   GPTQ_CHECK_LAUNCH();
   meta_kernel<<<cdiv(m * ng, 256), 256, 0, st>>>(scalesP, zerosP, m, ng, sgn, scales, zeros);
   GPTQ_CHECK_LAUNCH();
