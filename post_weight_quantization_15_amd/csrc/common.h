@@ -97,8 +97,8 @@ gptq_status launch_grid_in(const float* s_in, const uint8_t* z_in, int64_t m,
                            hipStream_t st);
 gptq_status launch_init_work(const void* W, gptq_dtype dt, int64_t m,
                              int64_t d, int64_t ldw, const int32_t* perm,
-                             const uint8_t* dead, float* WT, int32_t* pinv,
-                             hipStream_t st);
+                             const uint8_t* dead, bool ident, float* WT,
+                             int32_t* pinv, hipStream_t st);
 // RL[blk] = R's diagonal block blk (blocks of bi <= 128 columns) in the chain
 // kernel's lane order, 128 x 128 floats per block.
 gptq_status launch_rbt(const float* R, int64_t d, int bi, float* RL,

@@ -193,7 +193,7 @@ gptq_status enqueue_columns(const void* W, gptq_dtype w_dtype, int64_t m,
                             const float* Ru, const int32_t* pu,
                             const uint8_t* du, const QuantWs& q,
                             uint32_t* qweight, float* scales, uint8_t* zeros,
-                            int32_t* g_idx, float* w_hat, hipStream_t st) {
+                            int32_t* g_idx, float* w_hat, bool ident, hipStream_t st) {
   gptq_status s;
   int tk = trace_begin(st, GPTQ_TRACE_OTHER);
   const int64_t gsize = p->group_size;
@@ -212,7 +212,7 @@ gptq_status enqueue_columns(const void* W, gptq_dtype w_dtype, int64_t m,
                               sym, q.scalesP, q.zerosP, st)) != GPTQ_OK)
       return s;
   }
-  if ((s = launch_init_work(W, w_dtype, m, d, ldw, pu, du, q.WT, q.pinv, st)) != GPTQ_OK)
+  if ((s = launch_init_work(W, w_dtype, m, d, ldw, pu, du, ident, q.WT, q.pinv, st)) != GPTQ_OK)
     return s;
   const int bi = internal_block(d, p);
   if ((s = launch_rbt(Ru, d, bi, q.RbT, st)) != GPTQ_OK) return s;
@@ -518,7 +518,7 @@ gptq_status gptq_quantize_layer(const void* W, gptq_dtype w_dtype, int64_t m,
   hipStream_t st = static_cast<hipStream_t>(stream);
   if (!factor_inside)
     return enqueue_columns(W, w_dtype, m, d, ldw, p, R, perm, dead, q, qweight,
-                           scales, zeros, g_idx, w_hat, st);
+                           scales, zeros, g_idx, w_hat, false, st);
   // The whole layer is enqueued behind each damping attempt and the flag read
   // once at the end; a failed attempt's outputs are recomputed.
   double damp = 0.0;
@@ -527,8 +527,10 @@ gptq_status gptq_quantize_layer(const void* W, gptq_dtype w_dtype, int64_t m,
     if ((s = enqueue_factor(S, n, d, p->percdamp, p->act_order, attempt, q.R,
                             q.perm, q.dead, q.f, st)) != GPTQ_OK)
       return s;
+    // the order computed here is the identity without act-order
     if ((s = enqueue_columns(W, w_dtype, m, d, ldw, p, q.R, q.perm, q.dead, q,
-                             qweight, scales, zeros, g_idx, w_hat, st)) != GPTQ_OK)
+                             qweight, scales, zeros, g_idx, w_hat, p->act_order == 0,
+                             st)) != GPTQ_OK)
       return s;
     bool ok = false;
     if ((s = read_factor_outcome(q.f, st, &ok, &damp)) != GPTQ_OK) return s;

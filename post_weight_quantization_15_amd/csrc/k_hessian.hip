@@ -502,37 +502,43 @@ __global__ __launch_bounds__(256) void hessian_reduce_kernel(
   const bool diag = ti == tj;
   if (diag && wv == 2) return;
   const int wa = wv >> 1, wb = wv & 1;
-  const int tid = threadIdx.x, v = tid >> 6, lane = tid & 63;
-  const int row = 4 * (lane >> 4) + v;
+  // thread t sums the eight consecutive partial values 8t .. 8t + 7 of the
+  // band (accumulator register b8 * 4 + v, lanes l0 .. l0 + 7): eight
+  // consecutive columns of one row
+  const int tid = threadIdx.x;
+  const int e0 = 8 * tid, bv = e0 >> 6, l0 = e0 & 63;
+  const int row = 4 * (l0 >> 4) + (bv & 3);
+  const int col0 = 16 * (bv >> 2) + (l0 & 15);
   const int64_t i0 = int64_t(ti) * kSup + 128 * wa + 16 * a;
   const int64_t j0 = int64_t(tj) * kSup + 128 * wb;
   const int64_t i = i0 + row;
   const int64_t ntiles = upper_tiles(nt);
-  const float* src = part + (L * 4 + wv) * kSubElems + a * 8 * 4 * 64 + v * 64 + lane;
+  const float* src = part + (L * 4 + wv) * kSubElems + a * 8 * 4 * 64 + e0;
   const int64_t sstride = ntiles * 4 * kSubElems;
-  // the eight column blocks' sums advance together, four splits per batch
-  // of loads (the additions keep split order)
+  // four splits per batch of 16-byte loads (the additions keep split order)
   double sum[8] = {0.0, 0.0, 0.0, 0.0, 0.0, 0.0, 0.0, 0.0};
   for (int s0 = 0; s0 < nsplit; s0 += 4) {
-    float pv[4][8];
+    f32x4 pv[4][2];
 #pragma unroll
     for (int u = 0; u < 4; ++u)
 #pragma unroll
-      for (int b = 0; b < 8; ++b)
-        pv[u][b] = (s0 + u < nsplit) ? src[(s0 + u) * sstride + b * 4 * 64] : 0.0f;
+      for (int h = 0; h < 2; ++h)
+        pv[u][h] = (s0 + u < nsplit)
+                       ? *reinterpret_cast<const f32x4*>(src + (s0 + u) * sstride + 4 * h)
+                       : f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int u = 0; u < 4; ++u)
 #pragma unroll
-      for (int b = 0; b < 8; ++b)
-        if (s0 + u < nsplit) sum[b] += pv[u][b];
+      for (int k = 0; k < 8; ++k)
+        if (s0 + u < nsplit) sum[k] += pv[u][k >> 2][k & 3];
   }
 #pragma unroll
-  for (int b = 0; b < 8; ++b) {
-    const int col = 16 * b + (lane & 15);
+  for (int k = 0; k < 8; ++k) {
+    const int col = col0 + k;
     const int64_t j = j0 + col;
     float nv = 0.f;
     if (i < d && j < d && (!diag || i <= j)) {
-      nv = static_cast<float>(static_cast<double>(S[i * d + j]) + sum[b]);
+      nv = static_cast<float>(static_cast<double>(S[i * d + j]) + sum[k]);
       S[i * d + j] = nv;
     }
     band[row][col] = nv;

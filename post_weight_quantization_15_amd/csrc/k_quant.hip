@@ -79,29 +79,62 @@ __global__ void pinv_kernel(const int32_t* __restrict__ perm, int64_t d,
   if (j < d) pinv[perm[j]] = static_cast<int32_t>(j);
 }
 
-// WT[j][r] = dead[perm[j]] ? 0 : W[r][perm[j]]  via 64x64 LDS tiles.
-template <class T>
+// WT[j][r] = dead[perm[j]] ? 0 : W[r][perm[j]]  via 64x64 LDS tiles.  Thread
+// (row y = t / 4, quarter x = t % 4) reads columns 16x..16x+15 of row y (two
+// 16-byte loads of bf16 when the order is the identity and the row allows
+// it), then writes 16 consecutive rows of one column as four 16-byte stores
+// (VEC: m % 4 == 0 and WT 16-byte aligned).
+template <class T, bool VEC>
 __global__ __launch_bounds__(256) void init_work_kernel(
     const T* __restrict__ W, int64_t m, int64_t d, int64_t ldw,
     const int32_t* __restrict__ perm, const uint8_t* __restrict__ dead,
-    float* __restrict__ WT) {
-  __shared__ float tile[64][65];
+    int ident, float* __restrict__ WT) {
+  __shared__ float tile[64][65];       // [row][column]
   const int64_t r0 = int64_t(blockIdx.x) * 64, j0 = int64_t(blockIdx.y) * 64;
-  const int lx = threadIdx.x & 63, ly = threadIdx.x >> 6;
-  const int64_t j = j0 + lx;
-  int64_t src = -1;
-  if (j < d) {
-    const int32_t p = perm[j];
-    if (!dead[p]) src = p;
+  const int t = threadIdx.x, y = t >> 2, x = t & 3;
+  const int64_t r = r0 + y;
+  const int64_t jb = j0 + 16 * x;
+  bool wide = false;
+  if constexpr (sizeof(T) == 2) {
+    wide = ident && r < m && jb + 16 <= d &&
+           (reinterpret_cast<uintptr_t>(W + r * ldw + jb) & 15) == 0;
   }
-  for (int y = ly; y < 64; y += 4) {
-    const int64_t r = r0 + y;
-    tile[y][lx] = (r < m && src >= 0) ? to_f32(W[r * ldw + src]) : 0.0f;
+  if (wide) {
+    const u32x4* p = reinterpret_cast<const u32x4*>(W + r * ldw + jb);
+    const u32x4 a = p[0], b = p[1];
+    const uint32_t wv[8] = {a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const int64_t j = jb + 2 * u;
+      tile[y][16 * x + 2 * u] = dead[j] ? 0.0f : __uint_as_float(wv[u] << 16);
+      tile[y][16 * x + 2 * u + 1] = dead[j + 1] ? 0.0f : __uint_as_float(wv[u] & 0xffff0000u);
+    }
+  } else {
+#pragma unroll
+    for (int u = 0; u < 16; ++u) {
+      const int64_t j = jb + u;
+      float v = 0.0f;
+      if (r < m && j < d) {
+        const int32_t p = ident ? static_cast<int32_t>(j) : perm[j];
+        if (!dead[p]) v = to_f32(W[r * ldw + p]);
+      }
+      tile[y][16 * x + u] = v;
+    }
   }
   __syncthreads();
-  for (int y = ly; y < 64; y += 4) {
-    const int64_t jj = j0 + y, r = r0 + lx;
-    if (jj < d && r < m) WT[jj * m + r] = tile[lx][y];
+  // column jj = t / 4 of the tile, rows 16x..16x+15
+  const int64_t j = j0 + y;
+  if (j >= d) return;
+  float* dst = WT + j * m + r0 + 16 * x;
+  if (VEC && r0 + 16 * x + 16 <= m) {
+#pragma unroll
+    for (int u = 0; u < 4; ++u)
+      reinterpret_cast<f32x4*>(dst)[u] = f32x4{tile[16 * x + 4 * u][y], tile[16 * x + 4 * u + 1][y],
+                                               tile[16 * x + 4 * u + 2][y], tile[16 * x + 4 * u + 3][y]};
+  } else {
+#pragma unroll
+    for (int u = 0; u < 16; ++u)
+      if (r0 + 16 * x + u < m) dst[u] = tile[16 * x + u][y];
   }
 }
 
@@ -277,15 +310,20 @@ gptq_status launch_grid_in(const float* s_in, const uint8_t* z_in, int64_t m,
 
 gptq_status launch_init_work(const void* W, gptq_dtype dt, int64_t m,
                              int64_t d, int64_t ldw, const int32_t* perm,
-                             const uint8_t* dead, float* WT, int32_t* pinv,
-                             hipStream_t st) {
+                             const uint8_t* dead, bool ident, float* WT,
+                             int32_t* pinv, hipStream_t st) {
   pinv_kernel<<<cdiv(d, 256), 256, 0, st>>>(perm, d, pinv);
   GPTQ_CHECK_LAUNCH();
   const dim3 grid(cdiv(m, 64), cdiv(d, 64));
-  if (dt == GPTQ_F32)
-    init_work_kernel<float><<<grid, 256, 0, st>>>(static_cast<const float*>(W), m, d, ldw, perm, dead, WT);
-  else
-    init_work_kernel<uint16_t><<<grid, 256, 0, st>>>(static_cast<const uint16_t*>(W), m, d, ldw, perm, dead, WT);
+  const bool vec = m % 4 == 0 && reinterpret_cast<uintptr_t>(WT) % 16 == 0;
+#define GPTQ_INIT(TY, V) init_work_kernel<TY, V><<<grid, 256, 0, st>>>( \
+      static_cast<const TY*>(W), m, d, ldw, perm, dead, ident ? 1 : 0, WT)
+  if (dt == GPTQ_F32) {
+    if (vec) GPTQ_INIT(float, true); else GPTQ_INIT(float, false);
+  } else {
+    if (vec) GPTQ_INIT(uint16_t, true); else GPTQ_INIT(uint16_t, false);
+  }
+#undef GPTQ_INIT
   GPTQ_CHECK_LAUNCH();
   return GPTQ_OK;
 }
