@@ -407,9 +407,11 @@ __global__ __launch_bounds__(kThreads) void hessian_bf16_kernel(
   // work item of this workgroup (see blocked_tile)
   const int64_t ntiles = upper_tiles(nt);
   const int64_t nitems = ntiles * nsplit;
-  const int64_t per_xcd = (nitems + kXcd - 1) / kXcd;
+  // rounds of kCUs workgroups take consecutive runs of the list, XCD x the
+  // x-th run of kCUs / kXcd items of each round
   const int64_t w = blockIdx.x;
-  const int64_t item = (w % kXcd) * per_xcd + w / kXcd;
+  constexpr int64_t kPer = kCUs / kXcd;
+  const int64_t item = (w / kCUs) * kCUs + (w % kXcd) * kPer + (w / kXcd) % kPer;
   if (item >= nitems) return;
   const int split = static_cast<int>(item / ntiles);
   const int64_t t = item % ntiles;
@@ -686,8 +688,8 @@ gptq_status launch_hessian(float* S, int64_t d, const void* X, gptq_dtype dt,
   }
   const int nt = static_cast<int>((d + kSup - 1) / kSup);
   const SplitPlan p = plan_splits(d, n_tok, max_part);
-  const int64_t per_xcd = (upper_tiles(nt) * p.nsplit + kXcd - 1) / kXcd;
-  const dim3 grid(static_cast<unsigned>(kXcd * per_xcd));
+  const int64_t nitems = upper_tiles(nt) * p.nsplit;
+  const dim3 grid(static_cast<unsigned>((nitems + kCUs - 1) / kCUs * kCUs));
   hessian_bf16_kernel<true><<<grid, kThreads, 0, st>>>(
       static_cast<const uint16_t*>(X), ldx, n_tok, d, nt, p.ks, p.nsplit, S,
       static_cast<float*>(ws));
