@@ -1007,7 +1007,7 @@ gptq_status launch_trtri_r(int64_t d, const FactorWs& f, const double* T, int64_
 
 // Workgroups of the inverse's launches beside the factor: the step kernels
 // keep the rest of the chip.
-constexpr int64_t kSideWg = 96;
+constexpr int64_t kSideWg = 160;
 constexpr int64_t kAllWg = int64_t(1) << 30;
 
 // A second stream per device (default priority, created on first use) and

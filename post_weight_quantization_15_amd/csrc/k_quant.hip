@@ -172,7 +172,7 @@ __global__ void zero_fill_kernel(float* __restrict__ p, int64_t n) {
 // values to update are loaded before the product starts.  The narrow form
 // (NA = 2) doubles the workgroups of a launch, for launches whose wide
 // workgroups would leave part of the chip idle in their last round.
-constexpr int kDepth = 4;
+constexpr int kDepth = 8;
 
 // Elements c0..c0+N-1 of a row, the address clamped into [0, lim).  Lanes
 // whose columns fall past lim only feed outputs that are never stored, so
