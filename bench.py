@@ -394,7 +394,7 @@ def main():
     args = parse()
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); the layer "
-              "path has no multi-GPU mode in this build", file=sys.stderr)
+              "path has no multi-GPU mode", file=sys.stderr)
         sys.exit(2)
     import torch
     import post_weight_quantization_15_amd as gq
