@@ -424,6 +424,7 @@ __device__ inline GemmLds& gemm_lds() {
 template <bool B_KC, class FA, class FB>
 __device__ inline void tile_gemm(int64_t kbeg, int64_t kend, FA fa, FB fb,
                                  f64x4 acc[2][2]) {
+  static_assert(kKc == 32, "the fetch map below covers 64 x 32 operands per chunk");
   auto& As = gemm_lds().As;
   auto& Bs = gemm_lds().Bs;
   const int t = threadIdx.x;
